@@ -1,0 +1,21 @@
+"""CPU fp64 oracle for paged MLA decode -- TEST INFRASTRUCTURE ONLY.
+
+Only the test suite, the smoke check and the CPU-baseline leg of the bench may
+import or call anything in this package.  The product path (the HIP library
+and its Python binding) never does, and shares no code with it.
+"""
+
+from .mla_oracle import (  # noqa: F401
+    bf16_to_f64,
+    visible_tokens,
+    gather_latents,
+    attend_f64,
+    decode_ref,
+    decode_ref_rows,
+    decode_bruteforce,
+    softmax_weights,
+    explicit_heads,
+    absorb_query,
+    attend_chunks_and_merge,
+    merge_partials,
+)

@@ -1,0 +1,324 @@
+"""Pins of the fp64 oracle against facts that do not come from the oracle itself.
+
+Each check is chosen so that a plausible slip in the oracle (a dropped term, a
+wrong sign or index, a transposed operand, an off-by-one mask, a misread
+block table) breaks at least one of them; the last tests plant such slips and
+confirm they are caught.
+"""
+
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import mla_oracle
+from workloads import make_case, make_config_case, CONFIGS, PAGE, HEAD_DIM, V_DIM
+from casebuild import case_from_values, permute_pool, read_golden
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _tiny(seqlens, s_q, h_q, causal, seed, pool_factor=1.0):
+    return make_case(seqlens, s_q, h_q, causal, seed, pool_factor=pool_factor)
+
+
+# ---------------------------------------------------------------- (a) brute force
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("seqlens,s_q,h_q", [
+    ([1, 5], 1, 3),
+    ([63, 64], 2, 2),
+    ([65, 7, 130], 2, 2),
+    ([2, 1], 2, 1),
+])
+def test_bruteforce_matches_vectorized(seqlens, s_q, h_q, causal):
+    case = _tiny(seqlens, s_q, h_q, causal, seed=7, pool_factor=1.25)
+    o_ref, l_ref = oracle.decode_ref(case)
+    o_bf, l_bf = oracle.decode_bruteforce(case)
+    assert np.array_equal(np.isinf(l_ref), np.isinf(l_bf))
+    fin = np.isfinite(l_ref)
+    assert np.allclose(l_ref[fin], l_bf[fin], rtol=0, atol=1e-12)
+    assert np.allclose(o_ref, o_bf, rtol=0, atol=1e-12)
+
+
+# ---------------------------------------------------------------- (b) absorbed == explicit heads
+def test_absorbed_equals_explicit_heads():
+    rng = np.random.Generator(np.random.PCG64(11))
+    H, T = 4, 37
+    c = rng.standard_normal((T, 512))
+    r = rng.standard_normal((T, 64))
+    q_c = rng.standard_normal((H, 128))
+    q_r = rng.standard_normal((H, 64))
+    W_UK = rng.standard_normal((H, 128, 512)) / math.sqrt(512)
+    W_UV = rng.standard_normal((H, 128, 512)) / math.sqrt(512)
+    scale = 1.0 / math.sqrt(192.0)
+    o_exp, lse_exp = oracle.explicit_heads(c, r, q_c, q_r, W_UK, W_UV, scale)
+    q_abs = oracle.absorb_query(q_c, q_r, W_UK)  # [H, 576]
+    K = np.concatenate([c, r], axis=1)  # cache entries [c_t ; r_t]
+    out, lse = oracle.attend_f64(q_abs, K, [T] * H, scale)
+    o_abs = np.einsum("hdk,hk->hd", W_UV, out)
+    assert np.allclose(lse, lse_exp, rtol=1e-12, atol=0)
+    rel = np.linalg.norm(o_abs - o_exp) / np.linalg.norm(o_exp)
+    assert rel < 1e-10
+
+
+# ---------------------------------------------------------------- (c) paging
+def test_page_permutation_is_bitwise_invariant():
+    case = _tiny([130, 64, 1, 200], 2, 3, True, seed=3, pool_factor=1.25)
+    o1, l1 = oracle.decode_ref(case)
+    o2, l2 = oracle.decode_ref(permute_pool(case, seed=99))
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+def test_paged_equals_contiguous():
+    case = _tiny([130, 77], 1, 4, False, seed=5, pool_factor=1.25)
+    # rebuild the same logical cache contiguously: sequence b occupies pages
+    # in order, starting where the previous one ended
+    n = [(int(L) + PAGE - 1) // PAGE for L in case.cache_seqlens]
+    kv = np.zeros((sum(n), PAGE, HEAD_DIM), dtype=np.uint16)
+    bt = np.full_like(case.block_table, -1)
+    k = 0
+    for b, nb in enumerate(n):
+        for j in range(nb):
+            kv[k] = case.kv[case.block_table[b, j]]
+            bt[b, j] = k
+            k += 1
+    flat = type(case)(q=case.q, kv=kv, block_table=bt, cache_seqlens=case.cache_seqlens,
+                      softmax_scale=case.softmax_scale, causal=case.causal)
+    o1, l1 = oracle.decode_ref(case)
+    o2, l2 = oracle.decode_ref(flat)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+def test_unused_pages_and_tail_slots_do_not_matter():
+    clean = _tiny([70, 129], 1, 2, False, seed=8, pool_factor=1.25)
+    dirty = make_case([70, 129], 1, 2, False, 8, pool_factor=1.25,
+                      poison_unused=True, poison_tail=True)
+    o1, l1 = oracle.decode_ref(clean)
+    o2, l2 = oracle.decode_ref(dirty)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+# ---------------------------------------------------------------- (d) weights sum to one
+def test_weights_sum_to_one():
+    case = _tiny([300, 65], 2, 4, True, seed=21)
+    for b in range(case.batch):
+        P = oracle.softmax_weights(case, b)
+        assert np.allclose(P.sum(axis=1), 1.0, rtol=0, atol=1e-12)
+        assert np.all(P >= 0)
+
+
+# ---------------------------------------------------------------- closed forms
+def test_single_token_gives_its_value_and_score():
+    case = _tiny([1], 1, 5, False, seed=31)
+    o, l = oracle.decode_ref(case)
+    k0 = oracle.bf16_to_f64(case.kv[case.block_table[0, 0], 0])
+    q = oracle.bf16_to_f64(case.q[0, 0])
+    s0 = float(np.float32(case.softmax_scale)) * (q @ k0)
+    assert np.allclose(o[0, 0], np.broadcast_to(k0[:V_DIM], (5, V_DIM)), atol=1e-12)
+    assert np.allclose(l[0, 0], s0, atol=1e-12)
+
+
+def test_zero_scale_gives_mean_and_log_n():
+    case = _tiny([150], 1, 3, False, seed=41)
+    case.softmax_scale = 0.0
+    o, l = oracle.decode_ref(case)
+    K = oracle.gather_latents(case.kv, case.block_table[0], 150)
+    assert np.allclose(l, math.log(150), atol=1e-12)
+    assert np.allclose(o[0, 0], K[:, :V_DIM].mean(axis=0), atol=1e-12)
+
+
+def test_identical_tokens():
+    rng = np.random.Generator(np.random.PCG64(51))
+    tok = np.round(rng.standard_normal(HEAD_DIM) * 4) / 4  # bf16-exact
+    kv = np.broadcast_to(tok, (2, PAGE, HEAD_DIM)).astype(np.float32)
+    q = (np.round(rng.standard_normal((1, 1, 2, HEAD_DIM)) * 4) / 4).astype(np.float32)
+    case = case_from_values(q, kv, [[1, 0]], [100], 0.125, False)
+    o, l = oracle.decode_ref(case)
+    for h in range(2):
+        s = 0.125 * float(q[0, 0, h].astype(np.float64) @ tok)
+        assert abs(l[0, 0, h] - (s + math.log(100))) < 1e-12
+        assert np.allclose(o[0, 0, h], tok[:V_DIM], atol=1e-12)
+
+
+def test_identical_queries_give_identical_rows():
+    case = _tiny([90], 1, 4, False, seed=61)
+    case.q[0, 0, 1:] = case.q[0, 0, 0]
+    o, l = oracle.decode_ref(case)
+    for h in range(1, 4):
+        assert np.array_equal(o[0, 0, h], o[0, 0, 0]) and l[0, 0, h] == l[0, 0, 0]
+
+
+def test_value_all_ones_gives_ones():
+    case = _tiny([333, 20], 2, 3, True, seed=71)
+    one_bits = np.uint16(0x3F80)  # bf16 1.0
+    case.kv[:, :, :V_DIM] = one_bits
+    o, _ = oracle.decode_ref(case)
+    assert np.allclose(o, 1.0, atol=1e-12)
+
+
+def test_empty_sequence_convention():
+    case = _tiny([0, 5], 1, 2, False, seed=81)
+    o, l = oracle.decode_ref(case)
+    assert np.all(o[0] == 0.0) and np.all(np.isneginf(l[0]))
+    assert np.all(np.isfinite(l[1]))
+
+
+# ---------------------------------------------------------------- causal alignment
+def test_causal_row_equals_shorter_decode():
+    L = 150
+    case = _tiny([L], 2, 3, True, seed=91)
+    o, l = oracle.decode_ref(case)
+    for i in range(2):
+        single = type(case)(q=case.q[:, i:i + 1].copy(), kv=case.kv, block_table=case.block_table,
+                            cache_seqlens=np.array([L - 1 + i], dtype=np.int32),
+                            softmax_scale=case.softmax_scale, causal=False)
+        o1, l1 = oracle.decode_ref(single)
+        assert np.allclose(o[:, i], o1[:, 0], atol=1e-12)
+        assert np.allclose(l[:, i], l1[:, 0], atol=1e-12)
+
+
+def test_single_query_causal_equals_noncausal():
+    a = _tiny([77, 300], 1, 2, True, seed=101)
+    b = _tiny([77, 300], 1, 2, False, seed=101)
+    oa, la = oracle.decode_ref(a)
+    ob, lb = oracle.decode_ref(b)
+    assert np.array_equal(oa, ob) and np.array_equal(la, lb)
+
+
+# ---------------------------------------------------------------- split + merge
+@pytest.mark.parametrize("seed", [1, 2, 3])
+def test_split_and_merge_equals_unsplit(seed):
+    rng = np.random.Generator(np.random.PCG64(seed))
+    T, R = 257, 6
+    Q = rng.standard_normal((R, HEAD_DIM))
+    K = rng.standard_normal((T, HEAD_DIM))
+    n_rows = rng.integers(0, T + 1, size=R)
+    n_rows[0] = T
+    n_rows[1] = 0
+    scale = 1.0 / math.sqrt(192)
+    o_full, l_full = oracle.attend_f64(Q, K, n_rows, scale)
+    cuts = sorted(set([0, T] + list(rng.integers(1, T, size=5))))
+    o_m, l_m = oracle.attend_chunks_and_merge(Q, K, n_rows, scale, cuts)
+    assert np.array_equal(np.isinf(l_full), np.isinf(l_m))
+    fin = np.isfinite(l_full)
+    assert np.allclose(l_full[fin], l_m[fin], atol=1e-12)
+    assert np.allclose(o_full, o_m, atol=1e-12)
+
+
+# ---------------------------------------------------------------- golden worked examples
+def test_golden_two_token_example():
+    vals, _ = read_golden(os.path.join(GOLDEN, "two_token_example.txt"))
+    kv = np.zeros((1, PAGE, HEAD_DIM), dtype=np.float32)
+    kv[0, 0, 1] = 4.0
+    kv[0, 1, 0] = 1.0
+    kv[0, 1, 2] = 2.0
+    q = np.zeros((1, 1, 1, HEAD_DIM), dtype=np.float32)
+    q[0, 0, 0, 0] = 1.0
+    case = case_from_values(q, kv, [[0]], [2], math.log(3.0), False)
+    for fn in (oracle.decode_ref, oracle.decode_bruteforce):
+        o, l = fn(case)
+        o = o[0, 0, 0]
+        assert abs(o[0] - vals["out_0"]) < 1e-7
+        assert abs(o[1] - vals["out_1"]) < 1e-7
+        assert abs(o[2] - vals["out_2"]) < 1e-7
+        assert np.all(np.abs(o[3:]) <= vals["out_rest"] + 1e-12)
+        assert abs(l[0, 0, 0] - vals["lse"]) < 1e-7
+
+
+def test_golden_causal_example():
+    vals, _ = read_golden(os.path.join(GOLDEN, "causal_example.txt"))
+    kv = np.zeros((1, PAGE, HEAD_DIM), dtype=np.float32)
+    for t in range(3):
+        kv[0, t, t] = t + 1.0
+    q = np.zeros((1, 2, 1, HEAD_DIM), dtype=np.float32)
+    case = case_from_values(q, kv, [[0]], [3], 1.0, True)
+    for fn in (oracle.decode_ref, oracle.decode_bruteforce):
+        o, l = fn(case)
+        for i in range(2):
+            for d in range(3):
+                assert abs(o[0, i, 0, d] - vals[f"q{i}_out_{d}"]) < 1e-12
+            assert abs(l[0, i, 0] - vals[f"q{i}_lse"]) < 1e-12
+
+
+def test_golden_kv_bytes_per_token():
+    _, rows = read_golden(os.path.join(GOLDEN, "kv_bytes_per_token.txt"))
+    assert len(rows) == 3
+    for name, layers, per_layer, nbytes, printed_kb in rows:
+        total = int(layers) * int(per_layer) * int(nbytes)
+        assert total // 1000 == int(printed_kb), name  # printed figures are truncated
+    # the MLA row is exactly the oracle's per-token geometry
+    assert int(rows[0][2]) == HEAD_DIM and int(rows[0][3]) == 2
+
+
+# ---------------------------------------------------------------- workloads
+def test_config_shapes_and_tables():
+    case = make_config_case(2)
+    spec = CONFIGS[2]
+    assert case.q.shape == (8, 1, 16, HEAD_DIM)
+    L = case.cache_seqlens
+    assert np.all((L >= 1024) & (L <= 4096))
+    n = (L + PAGE - 1) // PAGE
+    used = np.concatenate([case.block_table[b, :n[b]] for b in range(8)])
+    assert len(set(used.tolist())) == len(used)  # no page shared
+    assert case.num_pages == math.ceil(n.sum() * spec.pool_factor)
+    for b in range(8):
+        assert np.all(case.block_table[b, n[b]:] == -1)
+    again = make_config_case(2)
+    assert np.array_equal(again.kv, case.kv) and np.array_equal(again.q, case.q)
+
+
+# ---------------------------------------------------------------- planted mistakes
+def test_planted_mask_off_by_one_is_caught(monkeypatch):
+    """A causal mask shifted by one breaks the hand-derived causal example."""
+    good = mla_oracle.visible_tokens
+    monkeypatch.setattr(mla_oracle, "visible_tokens",
+                        lambda L, s_q, i, c: good(L, s_q, i, c) - (1 if c else 0))
+    with pytest.raises(AssertionError):
+        test_golden_causal_example()
+
+
+def test_planted_dropped_rope_is_caught(monkeypatch):
+    """Scores that skip the 64 rotary dims disagree with the brute force."""
+    good = mla_oracle.attend_f64
+
+    def bad(Q, K, n_rows, scale, return_p=False):
+        K2 = np.array(K, dtype=np.float64)
+        K2[:, V_DIM:] = 0.0
+        res = good(Q, K2, n_rows, scale, return_p=True)
+        P = res[2]
+        out = P @ np.asarray(K, dtype=np.float64)[:, :V_DIM]
+        return (out, res[1], P) if return_p else (out, res[1])
+
+    monkeypatch.setattr(mla_oracle, "attend_f64", bad)
+    with pytest.raises(AssertionError):
+        test_bruteforce_matches_vectorized([65, 7, 130], 2, 2, False)
+
+
+def test_planted_page_misread_is_caught(monkeypatch):
+    """Reading physical page j instead of block_table[b, j] breaks invariance."""
+    def bad_gather(kv_bits, block_row, L):
+        L = int(L)
+        n_pages = (L + PAGE - 1) // PAGE
+        lat = kv_bits[np.arange(n_pages)].reshape(n_pages * PAGE, HEAD_DIM)[:L]
+        return mla_oracle.bf16_to_f64(lat)
+
+    monkeypatch.setattr(mla_oracle, "gather_latents", bad_gather)
+    with pytest.raises(AssertionError):
+        test_page_permutation_is_bitwise_invariant()
+
+
+def test_planted_transposed_value_is_caught(monkeypatch):
+    """Weighting the rotary tail instead of the latent breaks V == 1."""
+    good = mla_oracle.attend_f64
+
+    def bad(Q, K, n_rows, scale, return_p=False):
+        res = good(Q, K, n_rows, scale, return_p=True)
+        K = np.asarray(K, dtype=np.float64)
+        out = res[2] @ np.concatenate([K[:, 64:], K[:, :64]], axis=1)[:, :V_DIM]
+        return (out, res[1], res[2]) if return_p else (out, res[1])
+
+    monkeypatch.setattr(mla_oracle, "attend_f64", bad)
+    with pytest.raises(AssertionError):
+        test_value_all_ones_gives_ones()
