@@ -1,0 +1,304 @@
+#!/usr/bin/env python3
+"""Benchmark of one paged MLA decode step on one MI355X.
+
+A step is the whole hot path over one batch: split-KV schedule
+(mla_get_metadata), decode (mla_decode_paged) and combine (mla_combine).
+Inputs are seeded synthetic workloads (workloads.CONFIGS), resident in HBM
+before timing starts; R replicas of the cache / queries / tables rotate so
+that consecutive steps never hit the 256 MB Infinity Cache with the same KV.
+Steps are replayed through a captured HIP graph (no memset nodes), so host
+launch overhead does not enter the GPU time.
+
+Prints ONE JSON line (rank 0, N = 1).  `value` is the whole-step throughput
+in algorithmic HBM bytes per second; the roofline object is for the decode
+kernel, timed with HIP events on the stream it runs on.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2]
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+BF16_PEAK_TFLOPS = 2516.6  # MI355X dense bf16 MFMA, published (2.5 PFLOP/s)
+METRIC = "paged MLA decode achieved HBM GB/s and bf16 TFLOPS (fraction of roofline)"
+WORKLOAD_NAMES = {
+    1: "tiny_decode",
+    2: "memory_bound_decode",
+    3: "compute_bound_decode",
+    4: "multi_token_causal_decode",
+    5: "skewed_long_context_decode",
+}
+
+
+def algorithmic_work(case):
+    """Bytes the method must move and flops it must do (each visible KV token
+    read once: one latent serves every head)."""
+    L = case.cache_seqlens.astype(np.int64)
+    b, s_q, h_q = case.batch, case.s_q, case.h_q
+    R = s_q * h_q
+    pages = (L + 63) // 64
+    nbytes = (1152 * L.sum() + 1152 * b * R + 1024 * b * R + 4 * b * R + 4 * pages.sum() + 4 * b)
+    vis = 0
+    for i in range(s_q):
+        n = (L - s_q + 1 + i) if case.causal else L
+        vis += np.clip(n, 0, L).sum()
+    flops = 2 * (576 + 512) * h_q * vis
+    return int(nbytes), int(flops)
+
+
+def cpu_baseline(case, budget_s=20.0, min_s=10.0):
+    """Time the oracle (as it stands) on a bounded sample of the workload."""
+    import oracle
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    L = case.cache_seqlens.astype(np.int64)
+    order = list(range(case.batch))
+    # estimate per-batch cost by work and take batches until the budget
+    t0 = time.perf_counter()
+    oracle.decode_ref(case, batches=[order[0]])
+    first = time.perf_counter() - t0
+    per_tok = first / max(1, int(L[order[0]]))
+    chosen, est = [], 0.0
+    for b in order:
+        c = per_tok * max(1, int(L[b]))
+        if chosen and est + c > budget_s:
+            break
+        chosen.append(b)
+        est += c
+    # repeat the sample until about min_s of CPU work has been timed
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        oracle.decode_ref(case, batches=chosen)
+        reps += 1
+        if time.perf_counter() - t0 >= min_s:
+            break
+    dt = (time.perf_counter() - t0) / reps
+    sub = type(case)(q=case.q[chosen], kv=case.kv, block_table=case.block_table[chosen],
+                     cache_seqlens=case.cache_seqlens[chosen], softmax_scale=case.softmax_scale,
+                     causal=case.causal)
+    nbytes, flops = algorithmic_work(sub)
+    return {
+        "value": round(nbytes / dt / 1e9, 4),
+        "unit": "GB/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"fp64 numpy oracle over {len(chosen)} of {case.batch} sequences "
+                  f"({int(L[chosen].sum())} cached tokens), {reps} timed pass(es) of "
+                  f"{dt:.3f} s each; {flops / dt / 1e9:.2f} GFLOP/s",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--replicas", type=int, default=0, help="0 = enough to exceed 1 GiB")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: the decode path runs on a single MI355X "
+              "(multi-GPU sharding is described in DESIGN.md, not built)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import mla_paged_kv_06_amd as mla
+    from workloads import CONFIGS, make_config_case
+
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    mla.load_library()
+    dev = torch.device("cuda:0")
+    k = args.config
+    spec = CONFIGS[k]
+    case = make_config_case(k)
+    nbytes, flops = algorithmic_work(case)
+    print(f"# workload {k} ({spec.name}): batch {case.batch} s_q {case.s_q} h_q {case.h_q} "
+          f"sum L {int(case.cache_seqlens.sum())} pool {case.num_pages} pages; "
+          f"{nbytes / 1e6:.2f} MB, {flops / 1e9:.2f} GFLOP per step", file=sys.stderr, flush=True)
+
+    footprint = case.kv.nbytes + case.q.nbytes + case.block_table.nbytes
+    R = args.replicas or max(2, math.ceil((1 << 30) / footprint))
+    q0 = torch.from_numpy(case.q.view(np.int16)).to(dev).view(torch.bfloat16)
+    kv0 = torch.from_numpy(case.kv.view(np.int16)).to(dev).view(torch.bfloat16)
+    bt0 = torch.from_numpy(case.block_table).to(dev)
+    sl0 = torch.from_numpy(case.cache_seqlens).to(dev)
+    reps = [(q0, kv0, bt0, sl0)] + [(q0.clone(), kv0.clone(), bt0.clone(), sl0.clone())
+                                   for _ in range(R - 1)]
+    b, s_q, h_q = case.batch, case.s_q, case.h_q
+    parts = mla.num_partitions(s_q, h_q)
+    ws_bytes = mla.workspace_bytes(b, s_q, h_q)
+    bufs = []
+    for _ in range(R):
+        bufs.append(dict(
+            meta=torch.empty((parts, mla.META_INTS), dtype=torch.int32, device=dev),
+            splits=torch.empty((b + 1,), dtype=torch.int32, device=dev),
+            ws=torch.empty((ws_bytes,), dtype=torch.uint8, device=dev),
+            out=torch.empty((b, s_q, h_q, 512), dtype=torch.bfloat16, device=dev),
+            lse=torch.empty((b, s_q, h_q), dtype=torch.float32, device=dev)))
+    lib = mla.load_library()
+    import ctypes
+
+    def vp(t):
+        return ctypes.c_void_p(t.data_ptr())
+
+    def step(r):
+        q, kv, bt, sl = reps[r]
+        o = bufs[r]
+        st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        s1 = lib.mla_get_metadata(vp(sl), b, s_q, h_q, 0, vp(o["meta"]), vp(o["splits"]), st)
+        s2 = lib.mla_decode_paged(vp(q), vp(kv), vp(bt), vp(sl), b, s_q, h_q, case.num_pages,
+                                  case.max_pages, case.softmax_scale, int(case.causal),
+                                  vp(o["meta"]), vp(o["splits"]), 0, vp(o["ws"]), ws_bytes,
+                                  vp(o["out"]), vp(o["lse"]), st)
+        s3 = lib.mla_combine(vp(o["ws"]), ws_bytes, vp(o["splits"]), b, s_q, h_q, 0,
+                             vp(o["out"]), vp(o["lse"]), st)
+        if s1 or s2 or s3:
+            raise RuntimeError(f"library status {s1} {s2} {s3}")
+
+    # eager warmup (also sanity: every replica once)
+    for i in range(max(args.warmup, R)):
+        step(i % R)
+    torch.cuda.synchronize()
+
+    K = args.steps
+    timing = "hip-graph"
+
+    def capture(fn):
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            fn()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        return g
+
+    graph = None
+    if not args.no_graph:
+        try:
+            graph = capture(lambda: [step(r) for r in range(R)])
+        except Exception as e:  # capture not available: fall back to eager launches
+            print(f"# graph capture failed ({e}); timing eager launches", file=sys.stderr)
+            graph, timing = None, "eager"
+
+    # ---- timed region: exactly K whole steps (schedule + decode + combine)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    if graph is not None:
+        full, rem = divmod(K, R)
+        for _ in range(full):
+            graph.replay()
+        for r in range(rem):
+            step(r)
+    else:
+        for i in range(K):
+            step(i % R)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_per_step = elapsed * 1e3 / K
+
+    # ---- decode kernel duration: HIP events on the launch stream around
+    # back-to-back decode launches (one per replica, schedules already built)
+    def decodes():
+        for r in range(R):
+            q, kv, bt, sl = reps[r]
+            o = bufs[r]
+            st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+            st2 = lib.mla_decode_paged(vp(q), vp(kv), vp(bt), vp(sl), b, s_q, h_q, case.num_pages,
+                                       case.max_pages, case.softmax_scale, int(case.causal),
+                                       vp(o["meta"]), vp(o["splits"]), 0, vp(o["ws"]), ws_bytes,
+                                       vp(o["out"]), vp(o["lse"]), st)
+            if st2:
+                raise RuntimeError(f"decode status {st2}")
+
+    dgraph = None
+    if graph is not None:
+        try:
+            dgraph = capture(decodes)
+        except Exception as e:
+            print(f"# decode graph capture failed ({e})", file=sys.stderr)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    n_rep = max(3, K // R)
+    dec_ms = []
+    for _ in range(n_rep):
+        e0.record()
+        if dgraph is not None:
+            dgraph.replay()
+        else:
+            decodes()
+        e1.record()
+        torch.cuda.synchronize()
+        dec_ms.append(e0.elapsed_time(e1) / R)
+    dec_avg_ms = float(np.mean(dec_ms))
+
+    value = nbytes / (ms_per_step * 1e-3) / 1e9
+    achieved = nbytes / (dec_avg_ms * 1e-3) / 1e9
+    res = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": WORKLOAD_NAMES[k],
+            "batch": b, "s_q": s_q, "h_q": h_q, "head_dim": 576, "v_dim": 512, "page": 64,
+            "cache_seqlens": list(spec.lengths), "sum_seqlen": int(case.cache_seqlens.sum()),
+            "causal": bool(case.causal), "seed": 1000 + k, "replicas": R,
+            "timing": timing, "decode_launches_timed": n_rep * R,
+        },
+        "tflops": round(flops / (ms_per_step * 1e-3) / 1e12, 3),
+        "decode_kernel_ms": round(dec_avg_ms, 5),
+        "decode_tflops": round(flops / (dec_avg_ms * 1e-3) / 1e12, 3),
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": None,
+        },
+        "mfma_frac": round(flops / (dec_avg_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+    }
+    if not args.no_cpu_baseline:
+        print("# timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
+        res["cpu_baseline"] = cpu_baseline(case)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

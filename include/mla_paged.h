@@ -1,0 +1,156 @@
+/*
+ * mla_paged.h -- C ABI of the MI355X (gfx950) paged MLA decode library.
+ *
+ * Multi-head Latent Attention decode over a paged, variable-length bf16
+ * latent cache.  Sources for what is computed (by page and paragraph):
+ *   - FlashMLA release note (shoujike.com.cn): an MLA decode kernel tuned for
+ *     variable-length sequences (introduction); the cache is paged, bf16, with
+ *     64 tokens per block (paragraph on what was released); keys and values
+ *     are held as one compressed latent per token and widened at compute time
+ *     (paragraph on MLA core principles); exact softmax attention in the
+ *     FlashAttention line (acknowledgements paragraph).
+ *   - DeepSeek-V3 hardware paper summary (news.chathome.org), paragraph on
+ *     memory efficiency: the latent is shared by every attention head.
+ *   - Tom's Hardware FR article on FlashMLA, paragraph on the techniques:
+ *     block-based paging allocated on demand for variable-length sequences.
+ *
+ * The operation.  For sequence b with L = cache_seqlens[b] cached tokens and
+ * each query row (query token i < s_q, head h < h_q):
+ *     n      = L                       (non-causal)
+ *            = clamp(L - s_q + 1 + i, 0, L)   (causal: the s_q queries are
+ *              the last s_q cache positions; query i sees positions
+ *              0 .. L - s_q + i)
+ *     k_t    = kv_cache[block_table[b][t / 64]][t % 64][0:576]     (t < n)
+ *     s_t    = softmax_scale * dot(q[b][i][h][0:576], k_t)
+ *     lse    = ln(sum_t exp(s_t))                    (natural log)
+ *     out    = sum_t exp(s_t - lse) * k_t[0:512]     (the latent is the value)
+ * An empty row (n = 0) gives out = 0 and lse = -inf.  out is rounded once to
+ * bf16 (nearest-even); lse is float32.
+ *
+ * Dimensions are fixed: 576-value latent (512 latent + 64 rotary), 512-value
+ * output, 64-token pages, one latent head shared by every query head.
+ *
+ * Layouts (all row-major, contiguous, device memory, 16-byte aligned):
+ *   q             bf16  [batch][s_q][h_q][576]   query row r = i*h_q + h
+ *   kv_cache      bf16  [num_pages][64][576]
+ *   block_table   int32 [batch][max_pages]        entries < ceil(L/64) used
+ *   cache_seqlens int32 [batch]
+ *   out           bf16  [batch][s_q][h_q][512]
+ *   lse           fp32  [batch][s_q][h_q]
+ *
+ * Call sequence for one decode step (every call is asynchronous on `stream`):
+ *   mla_get_metadata(...)       once per step (depends only on cache_seqlens)
+ *   mla_decode_paged(...)       per layer
+ *   mla_combine(...)            per layer, after decode, same stream
+ *
+ * Ownership.  The caller allocates and frees every buffer; the library never
+ * allocates, frees or synchronizes.  Pointers must stay valid until the work
+ * queued on `stream` has finished.  The only library state is a per-device
+ * cache of the compute-unit count.
+ *
+ * Errors.  Host-visible arguments are checked before anything is launched; a
+ * failed check returns a status and launches nothing.  A failed launch
+ * returns MLA_ERR_HIP.  Device-side contents are preconditions that are not
+ * checked: every cache_seqlens[b] in [0, max_pages*64], and every used
+ * block_table entry in [0, num_pages).  No C++ exception crosses this ABI.
+ */
+#ifndef MLA_PAGED_H
+#define MLA_PAGED_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MLA_OK = 0,
+  MLA_ERR_INVALID_ARGUMENT = 1, /* null pointer, non-positive size, bad scale */
+  MLA_ERR_UNSUPPORTED = 2,      /* shape outside the supported limits below */
+  MLA_ERR_WORKSPACE_TOO_SMALL = 3,
+  MLA_ERR_HIP = 4               /* a HIP runtime call or launch failed */
+} mla_status_t;
+
+#define MLA_HEAD_DIM 576
+#define MLA_V_DIM 512
+#define MLA_PAGE_SIZE 64
+#define MLA_META_INTS 8      /* ints per partition in tile_metadata */
+#define MLA_MAX_BATCH 65536
+#define MLA_MAX_ROWS 2048    /* s_q * h_q */
+#define MLA_MAX_PARTS 4096   /* partitions of the key range (see below) */
+
+/*
+ * Number of key-range partitions used for `num_cus` compute units
+ * (0 = the current device's count).  Query rows are processed in groups of up
+ * to 64; the partitions times the row groups give about one workgroup per
+ * compute unit.  Returns 0 for invalid arguments.
+ */
+int32_t mla_num_partitions(int32_t s_q, int32_t h_q, int32_t num_cus);
+
+/* int32 entries of tile_metadata: mla_num_partitions(...) * MLA_META_INTS. */
+size_t mla_metadata_ints(int32_t s_q, int32_t h_q, int32_t num_cus);
+
+/*
+ * Bytes of workspace mla_decode_paged / mla_combine need: float32 partial
+ * outputs and log-sum-exps for sequences whose keys are split over several
+ * partitions, one slot per (sequence, split).
+ */
+size_t mla_workspace_bytes(int32_t batch, int32_t s_q, int32_t h_q, int32_t num_cus);
+
+/*
+ * Split-KV schedule.  Reads cache_seqlens on the device and writes
+ *   tile_metadata int32 [partitions][8]: per partition the half-open range of
+ *       (sequence, page) work it owns, {b_begin, page_begin, b_end, page_end,
+ *       first_split, units_per_partition, fixed_cost, total_units}, pages
+ *       counted in 64-token units (an empty sequence counts as one page that
+ *       holds nothing); first_split is the index, among the partitions that
+ *       share sequence b_begin, of this one; the last three describe the cut
+ *       (every sequence costs fixed_cost + its pages; partition p starts at
+ *       unit p * units_per_partition);
+ *   num_splits    int32 [batch + 1]: exclusive prefix over sequences of how
+ *       many partitions share each one (num_splits[batch] = slots used).
+ * Work is balanced by cutting the concatenation of every sequence's pages,
+ * each sequence charged a fixed extra cost, into equal shares.  One
+ * workgroup, asynchronous on `stream`.
+ */
+mla_status_t mla_get_metadata(const int32_t* cache_seqlens, int32_t batch, int32_t s_q,
+                              int32_t h_q, int32_t num_cus, int32_t* tile_metadata,
+                              int32_t* num_splits, hipStream_t stream);
+
+/*
+ * Decode.  Each workgroup walks its partition's pages, streams every 64-token
+ * latent page from HBM into LDS once, and runs Q.K^T and P.V on bf16 matrix
+ * cores with an online softmax.  Sequences owned by one partition are
+ * written straight to out/lse; the others write float32 partials into the
+ * workspace for mla_combine.  tile_metadata and num_splits must come from
+ * mla_get_metadata with the same cache_seqlens, batch, s_q, h_q and num_cus.
+ */
+mla_status_t mla_decode_paged(const void* q, const void* kv_cache, const int32_t* block_table,
+                              const int32_t* cache_seqlens, int32_t batch, int32_t s_q,
+                              int32_t h_q, int32_t num_pages, int32_t max_pages,
+                              float softmax_scale, int32_t causal, const int32_t* tile_metadata,
+                              const int32_t* num_splits, int32_t num_cus, void* workspace,
+                              size_t workspace_bytes, void* out, float* lse, hipStream_t stream);
+
+/*
+ * Combine.  For every sequence split over several partitions, merges the
+ * partials by log-sum-exp: lse = ln sum_s exp(lse_s), out = sum_s
+ * exp(lse_s - lse) o_s, rounded to bf16.  Partials with lse_s = -inf carry no
+ * weight; if every one is -inf the row is written as out = 0, lse = -inf.
+ * Sequences owned by one partition are left untouched.
+ */
+mla_status_t mla_combine(const void* workspace, size_t workspace_bytes, const int32_t* num_splits,
+                         int32_t batch, int32_t s_q, int32_t h_q, int32_t num_cus, void* out,
+                         float* lse, hipStream_t stream);
+
+/* Static, human-readable text of a status code. */
+const char* mla_status_string(mla_status_t status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_PAGED_H */

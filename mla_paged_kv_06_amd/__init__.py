@@ -1,0 +1,190 @@
+"""Python binding of libmla_paged.so: paged MLA decode on MI355X (gfx950).
+
+Argument marshalling only.  Every step of the decode (split-KV schedule,
+attention, combine) runs in the HIP kernels behind the C ABI declared in
+``include/mla_paged.h``; torch only provides device memory and the stream.
+If the shared library has not been built, every call raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+__all__ = [
+    "MlaError",
+    "HEAD_DIM",
+    "V_DIM",
+    "PAGE_SIZE",
+    "META_INTS",
+    "library_path",
+    "load_library",
+    "num_partitions",
+    "metadata_ints",
+    "workspace_bytes",
+    "get_metadata",
+    "decode_paged",
+    "combine",
+    "mla_decode",
+]
+
+HEAD_DIM = 576
+V_DIM = 512
+PAGE_SIZE = 64
+META_INTS = 8
+
+_PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+_LIB_NAME = "libmla_paged.so"
+_lib = None
+
+
+class MlaError(RuntimeError):
+    """A non-OK status from the C ABI."""
+
+    def __init__(self, fn: str, status: int, text: str):
+        super().__init__(f"{fn} failed: status {status} ({text})")
+        self.status = status
+
+
+def library_path() -> str:
+    return os.path.join(_PKG_DIR, _LIB_NAME)
+
+
+def load_library() -> ctypes.CDLL:
+    """Load the in-tree HIP library (built by ``python -m mla_paged_kv_06_amd.build``)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = library_path()
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"{path} is missing: build it with `python -m mla_paged_kv_06_amd.build` "
+            "(there is no fallback path)")
+    lib = ctypes.CDLL(path)
+    i32, sz, vp, f32 = ctypes.c_int32, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_float
+    lib.mla_num_partitions.argtypes = [i32, i32, i32]
+    lib.mla_num_partitions.restype = i32
+    lib.mla_metadata_ints.argtypes = [i32, i32, i32]
+    lib.mla_metadata_ints.restype = sz
+    lib.mla_workspace_bytes.argtypes = [i32, i32, i32, i32]
+    lib.mla_workspace_bytes.restype = sz
+    lib.mla_get_metadata.argtypes = [vp, i32, i32, i32, i32, vp, vp, vp]
+    lib.mla_get_metadata.restype = ctypes.c_int
+    lib.mla_decode_paged.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32, vp, vp,
+                                     i32, vp, sz, vp, vp, vp]
+    lib.mla_decode_paged.restype = ctypes.c_int
+    lib.mla_combine.argtypes = [vp, sz, vp, i32, i32, i32, i32, vp, vp, vp]
+    lib.mla_combine.restype = ctypes.c_int
+    lib.mla_status_string.argtypes = [ctypes.c_int]
+    lib.mla_status_string.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def _check(fn: str, status: int) -> None:
+    if status != 0:
+        text = load_library().mla_status_string(status).decode()
+        raise MlaError(fn, status, text)
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _ptr(t: Optional[torch.Tensor]) -> ctypes.c_void_p:
+    return ctypes.c_void_p(0 if t is None else t.data_ptr())
+
+
+def _need(t: torch.Tensor, name: str, dtype: torch.dtype, dims: int) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on the GPU")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.dim() != dims:
+        raise ValueError(f"{name} must have {dims} dims, got shape {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def num_partitions(s_q: int, h_q: int, num_cus: int = 0) -> int:
+    return int(load_library().mla_num_partitions(s_q, h_q, num_cus))
+
+
+def metadata_ints(s_q: int, h_q: int, num_cus: int = 0) -> int:
+    return int(load_library().mla_metadata_ints(s_q, h_q, num_cus))
+
+
+def workspace_bytes(batch: int, s_q: int, h_q: int, num_cus: int = 0) -> int:
+    return int(load_library().mla_workspace_bytes(batch, s_q, h_q, num_cus))
+
+
+def get_metadata(cache_seqlens: torch.Tensor, s_q: int, h_q: int, num_cus: int = 0,
+                 stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Split-KV schedule: returns ``(tile_metadata [parts, 8], num_splits [batch+1])``."""
+    _need(cache_seqlens, "cache_seqlens", torch.int32, 1)
+    batch = cache_seqlens.shape[0]
+    parts = num_partitions(s_q, h_q, num_cus)
+    if parts <= 0:
+        raise MlaError("mla_num_partitions", 1, "invalid arguments")
+    dev = cache_seqlens.device
+    meta = torch.empty((parts, META_INTS), dtype=torch.int32, device=dev)
+    splits = torch.empty((batch + 1,), dtype=torch.int32, device=dev)
+    _check("mla_get_metadata", load_library().mla_get_metadata(
+        _ptr(cache_seqlens), batch, s_q, h_q, num_cus, _ptr(meta), _ptr(splits), _stream(stream)))
+    return meta, splits
+
+
+def decode_paged(q: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Tensor,
+                 cache_seqlens: torch.Tensor, softmax_scale: float, causal: bool,
+                 tile_metadata: torch.Tensor, num_splits: torch.Tensor, num_cus: int = 0,
+                 workspace: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                 lse: Optional[torch.Tensor] = None, stream=None):
+    """Decode (without the combine).  Returns ``(out, lse, workspace)``."""
+    _need(q, "q", torch.bfloat16, 4)
+    _need(kv_cache, "kv_cache", torch.bfloat16, 3)
+    _need(block_table, "block_table", torch.int32, 2)
+    _need(cache_seqlens, "cache_seqlens", torch.int32, 1)
+    batch, s_q, h_q, d = q.shape
+    if d != HEAD_DIM or kv_cache.shape[1] != PAGE_SIZE or kv_cache.shape[2] != HEAD_DIM:
+        raise ValueError("q must be [b,s_q,h_q,576] and kv_cache [pages,64,576]")
+    if block_table.shape[0] != batch or cache_seqlens.shape[0] != batch:
+        raise ValueError("block_table / cache_seqlens batch mismatch")
+    dev = q.device
+    if out is None:
+        out = torch.empty((batch, s_q, h_q, V_DIM), dtype=torch.bfloat16, device=dev)
+    if lse is None:
+        lse = torch.empty((batch, s_q, h_q), dtype=torch.float32, device=dev)
+    need = workspace_bytes(batch, s_q, h_q, num_cus)
+    if workspace is None:
+        workspace = torch.empty((max(need, 16),), dtype=torch.uint8, device=dev)
+    _check("mla_decode_paged", load_library().mla_decode_paged(
+        _ptr(q), _ptr(kv_cache), _ptr(block_table), _ptr(cache_seqlens), batch, s_q, h_q,
+        kv_cache.shape[0], block_table.shape[1], float(softmax_scale), int(bool(causal)),
+        _ptr(tile_metadata), _ptr(num_splits), num_cus, _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _ptr(out), _ptr(lse), _stream(stream)))
+    return out, lse, workspace
+
+
+def combine(workspace: torch.Tensor, num_splits: torch.Tensor, batch: int, s_q: int, h_q: int,
+            out: torch.Tensor, lse: torch.Tensor, num_cus: int = 0, stream=None) -> None:
+    """Merge split partials into ``out`` / ``lse`` in place."""
+    _check("mla_combine", load_library().mla_combine(
+        _ptr(workspace), workspace.numel() * workspace.element_size(), _ptr(num_splits), batch,
+        s_q, h_q, num_cus, _ptr(out), _ptr(lse), _stream(stream)))
+
+
+def mla_decode(q, kv_cache, block_table, cache_seqlens, softmax_scale, causal, num_cus: int = 0,
+               stream=None):
+    """One full decode step: schedule, decode, combine.  Returns ``(out, lse)``."""
+    batch, s_q, h_q, _ = q.shape
+    meta, splits = get_metadata(cache_seqlens, s_q, h_q, num_cus, stream)
+    out, lse, ws = decode_paged(q, kv_cache, block_table, cache_seqlens, softmax_scale, causal,
+                                meta, splits, num_cus, stream=stream)
+    combine(ws, splits, batch, s_q, h_q, out, lse, num_cus, stream)
+    return out, lse

@@ -1,0 +1,184 @@
+// C ABI of the paged MLA decode library: argument checks, launch shapes,
+// status codes.  Declared in include/mla_paged.h.
+
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cmath>
+#include <cstddef>
+#include <cstdint>
+
+#include "mla_paged.h"
+#include "mla_device.h"
+
+extern "C" hipError_t mla_launch_sched(const int32_t* seqlens, int batch, int num_parts, int c0,
+                                       int32_t* meta, int32_t* splits, hipStream_t stream);
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_cu_count[kMaxDevices];
+
+// Compute units of the current device, cached per device.
+int device_cus() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
+  int v = g_cu_count[dev].load(std::memory_order_relaxed);
+  if (v > 0) return v;
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  g_cu_count[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
+bool rows_ok(int32_t s_q, int32_t h_q) {
+  if (s_q <= 0 || h_q <= 0) return false;
+  const long long R = (long long)s_q * h_q;
+  return R <= MLA_MAX_ROWS;
+}
+
+int row_groups_of(int R) { return (R + mla::kRowGroup - 1) / mla::kRowGroup; }
+
+// Query rows one workgroup holds: the smallest tuned size covering a row group.
+int rows_variant_of(int R) {
+  const int r = R < mla::kRowGroup ? R : mla::kRowGroup;
+  if (r <= 16) return 16;
+  if (r <= 32) return 32;
+  return 64;
+}
+
+// Fixed cost of one (sequence, partition) segment in page units: the query
+// load and the epilogue grow with the rows held.
+int fixed_cost_of(int R) { return 1 + rows_variant_of(R) / 32; }
+
+int parts_of(int32_t s_q, int32_t h_q, int32_t num_cus) {
+  if (!rows_ok(s_q, h_q) || num_cus < 0) return 0;
+  const int cus = num_cus > 0 ? num_cus : device_cus();
+  if (cus <= 0) return 0;
+  const int R = s_q * h_q;
+  int parts = cus / row_groups_of(R);
+  if (parts < 1) parts = 1;
+  if (parts > MLA_MAX_PARTS) parts = MLA_MAX_PARTS;
+  return parts;
+}
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// workspace: o_acc [slots][R][512] fp32, then lse_acc [slots][R] fp32
+size_t oacc_bytes(int batch, int R, int parts) {
+  return align_up((size_t)(batch + parts) * R * MLA_V_DIM * sizeof(float), 256);
+}
+size_t ws_bytes(int batch, int R, int parts) {
+  return oacc_bytes(batch, R, parts) + align_up((size_t)(batch + parts) * R * sizeof(float), 256);
+}
+
+}  // namespace
+
+extern "C" hipError_t mla_launch_decode(const mla::DecodeParams* prm, int rows_variant,
+                                        hipStream_t stream);
+extern "C" hipError_t mla_launch_combine(const float* o_acc, const float* lse_acc,
+                                         const int32_t* splits, int batch, int R, uint16_t* out,
+                                         float* lse, hipStream_t stream);
+
+extern "C" {
+
+int32_t mla_num_partitions(int32_t s_q, int32_t h_q, int32_t num_cus) {
+  return parts_of(s_q, h_q, num_cus);
+}
+
+size_t mla_metadata_ints(int32_t s_q, int32_t h_q, int32_t num_cus) {
+  return (size_t)parts_of(s_q, h_q, num_cus) * MLA_META_INTS;
+}
+
+size_t mla_workspace_bytes(int32_t batch, int32_t s_q, int32_t h_q, int32_t num_cus) {
+  if (batch <= 0 || batch > MLA_MAX_BATCH) return 0;
+  const int parts = parts_of(s_q, h_q, num_cus);
+  if (parts <= 0) return 0;
+  return ws_bytes(batch, s_q * h_q, parts);
+}
+
+mla_status_t mla_get_metadata(const int32_t* cache_seqlens, int32_t batch, int32_t s_q,
+                              int32_t h_q, int32_t num_cus, int32_t* tile_metadata,
+                              int32_t* num_splits, hipStream_t stream) {
+  if (!cache_seqlens || !tile_metadata || !num_splits) return MLA_ERR_INVALID_ARGUMENT;
+  if (batch <= 0 || s_q <= 0 || h_q <= 0 || num_cus < 0) return MLA_ERR_INVALID_ARGUMENT;
+  if (batch > MLA_MAX_BATCH || !rows_ok(s_q, h_q)) return MLA_ERR_UNSUPPORTED;
+  const int parts = parts_of(s_q, h_q, num_cus);
+  if (parts <= 0) return MLA_ERR_HIP;
+  const int c0 = fixed_cost_of(s_q * h_q);
+  hipError_t e = mla_launch_sched(cache_seqlens, batch, parts, c0, tile_metadata, num_splits, stream);
+  return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+mla_status_t mla_decode_paged(const void* q, const void* kv_cache, const int32_t* block_table,
+                              const int32_t* cache_seqlens, int32_t batch, int32_t s_q,
+                              int32_t h_q, int32_t num_pages, int32_t max_pages,
+                              float softmax_scale, int32_t causal, const int32_t* tile_metadata,
+                              const int32_t* num_splits, int32_t num_cus, void* workspace,
+                              size_t workspace_bytes, void* out, float* lse, hipStream_t stream) {
+  if (!q || !kv_cache || !block_table || !cache_seqlens || !tile_metadata || !num_splits ||
+      !workspace || !out || !lse)
+    return MLA_ERR_INVALID_ARGUMENT;
+  if (batch <= 0 || s_q <= 0 || h_q <= 0 || num_pages <= 0 || max_pages <= 0 || num_cus < 0)
+    return MLA_ERR_INVALID_ARGUMENT;
+  if (!std::isfinite(softmax_scale)) return MLA_ERR_INVALID_ARGUMENT;
+  if (batch > MLA_MAX_BATCH || !rows_ok(s_q, h_q)) return MLA_ERR_UNSUPPORTED;
+  if (((uintptr_t)q | (uintptr_t)kv_cache | (uintptr_t)out | (uintptr_t)workspace) & 15)
+    return MLA_ERR_INVALID_ARGUMENT;
+  const int parts = parts_of(s_q, h_q, num_cus);
+  if (parts <= 0) return MLA_ERR_HIP;
+  const int R = s_q * h_q;
+  if (workspace_bytes < ws_bytes(batch, R, parts)) return MLA_ERR_WORKSPACE_TOO_SMALL;
+
+  mla::DecodeParams prm;
+  prm.q = (const uint16_t*)q;
+  prm.kv = (const uint16_t*)kv_cache;
+  prm.block_table = block_table;
+  prm.seqlens = cache_seqlens;
+  prm.meta = tile_metadata;
+  prm.splits = num_splits;
+  prm.out = (uint16_t*)out;
+  prm.lse = lse;
+  prm.o_acc = (float*)workspace;
+  prm.lse_acc = (float*)((char*)workspace + oacc_bytes(batch, R, parts));
+  prm.batch = batch;
+  prm.s_q = s_q;
+  prm.h_q = h_q;
+  prm.R = R;
+  prm.max_pages = max_pages;
+  prm.num_parts = parts;
+  prm.row_groups = row_groups_of(R);
+  prm.causal = causal ? 1 : 0;
+  prm.scale_log2 = (float)((double)softmax_scale * 1.4426950408889634);
+  hipError_t e = mla_launch_decode(&prm, rows_variant_of(R), stream);
+  return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+mla_status_t mla_combine(const void* workspace, size_t workspace_bytes, const int32_t* num_splits,
+                         int32_t batch, int32_t s_q, int32_t h_q, int32_t num_cus, void* out,
+                         float* lse, hipStream_t stream) {
+  if (!workspace || !num_splits || !out || !lse) return MLA_ERR_INVALID_ARGUMENT;
+  if (batch <= 0 || s_q <= 0 || h_q <= 0 || num_cus < 0) return MLA_ERR_INVALID_ARGUMENT;
+  if (batch > MLA_MAX_BATCH || !rows_ok(s_q, h_q)) return MLA_ERR_UNSUPPORTED;
+  const int parts = parts_of(s_q, h_q, num_cus);
+  if (parts <= 0) return MLA_ERR_HIP;
+  const int R = s_q * h_q;
+  if (workspace_bytes < ws_bytes(batch, R, parts)) return MLA_ERR_WORKSPACE_TOO_SMALL;
+  const float* o_acc = (const float*)workspace;
+  const float* lse_acc = (const float*)((const char*)workspace + oacc_bytes(batch, R, parts));
+  hipError_t e = mla_launch_combine(o_acc, lse_acc, num_splits, batch, R, (uint16_t*)out, lse, stream);
+  return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+const char* mla_status_string(mla_status_t status) {
+  switch (status) {
+    case MLA_OK: return "ok";
+    case MLA_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case MLA_ERR_UNSUPPORTED: return "unsupported shape";
+    case MLA_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case MLA_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+}  // extern "C"

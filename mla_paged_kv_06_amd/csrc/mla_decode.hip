@@ -1,0 +1,503 @@
+// Paged MLA decode for gfx950 (CDNA4): page gather -> LDS, S^T = K Q^T and
+// O^T += V^T P^T on bf16 MFMA, online softmax in registers.
+//
+// What is computed (FlashMLA release note, paragraphs on MLA core principles
+// and on the released paged bf16 cache; DeepSeek-V3 hardware paper summary,
+// paragraph on memory efficiency): every query head attends over one shared
+// 576-value latent per token, the first 512 values of which are the value.
+// Because all heads read the same latent, the score and value products of a
+// page are dense contractions with one row per (query token, head) -- the
+// work that goes on the matrix cores.  The exact-softmax tiling with a
+// running max and sum follows the FlashAttention line the release note's
+// acknowledgements name; the layout below is our own for CDNA4.
+//
+// Workgroup = 4 waves (256 threads), one per SIMD; one workgroup per CU
+// (two 72 KiB page buffers fill most of the 160 KiB LDS).
+//
+// Per page (64 tokens) and wave:
+//   * the page is copied HBM -> LDS by global_load_lds (16 B per lane, 72
+//     wave-wide loads split over the 4 waves), double-buffered: page k+1 is
+//     in flight while page k is computed;
+//   * S^T[token][row] = sum_d K[token][d] Q[row][d]: MFMA 16x16x32 with the
+//     K tile (LDS, 16-byte reads) as A and the query rows (registers, loaded
+//     once per sequence) as B.  The accumulator gives each lane one query row
+//     (lane % 16) and 16 tokens, so the row max / sum needs only a 4-lane
+//     reduction and the weights are already laid out as the B operand of the
+//     next product;
+//   * O^T[col][row] += sum_t V[t][col] P[row][t]: MFMA 16x16x32 with V^T read
+//     by ds_read_b64_tr_b16 straight from the same LDS tile (the value is the
+//     first 512 values of the latent) and the bf16 weights as B.  Each lane
+//     again holds one query row, so the rescale of O is a per-lane scalar.
+//
+// Variants (query rows per workgroup; wave grid rows x cols):
+//   16 rows: 1 x 4 waves, each wave all 16 rows and 128 output columns
+//            (the score product is repeated per wave; it is cheap here);
+//   32 rows: 2 x 2;  64 rows: 4 x 1;  128 rows: 4 x 1 with 32 rows per wave.
+
+#include "mla_device.h"
+
+namespace mla {
+
+
+struct Item {
+  int b, j;
+};
+
+__device__ __forceinline__ bool item_before(Item a, int eb, int ej) {
+  return a.b < eb || (a.b == eb && a.j < ej);
+}
+
+// Wave-uniform value (kept in an SGPR, so loads indexed by it are scalar).
+__device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+// Barrier for LDS traffic only: unlike __syncthreads it does not wait for
+// outstanding global loads, so a page prefetch in flight keeps flying.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+__device__ __forceinline__ int page_slots(const int32_t* seqlens, int b) {
+  int L = uni(seqlens[b]);
+  int n = (L + kPage - 1) / kPage;
+  return n > 0 ? n : 1;
+}
+
+// Copy one 64-token page into an LDS tile.  The page is 8 blocks of 8 tokens
+// (9216 B each = 9 wave-wide 1 KiB loads); wave w copies blocks 2w and 2w+1.
+// Inside a block, load k, lane l fills LDS chunk 64 k + l of the block:
+// token t' = (64 k + l) / 72, physical chunk p = (64 k + l) % 72, which
+// holds logical chunk p ^ swz(t').  swz depends on t & 7 only, so the nine
+// per-lane source offsets are the same for every block.
+struct PageLoader {
+  int off[9];  // per-lane source byte offsets inside an 8-token block
+  __device__ __forceinline__ void init(int lane) {
+#pragma unroll
+    for (int k = 0; k < 9; ++k) {
+      const int pc = 64 * k + lane;
+      const int t = pc / kChunksPerRow;
+      const int p = pc - t * kChunksPerRow;
+      off[k] = t * kRowBytes + 16 * (p ^ swz(t));
+    }
+  }
+  __device__ __forceinline__ void issue(MLA_LDS char* tile, const char* page, int wave) const {
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk) {
+      const int base = (2 * wave + blk) * 8 * kRowBytes;  // == 9 KiB of LDS per block
+#pragma unroll
+      for (int k = 0; k < 9; ++k)
+        __builtin_amdgcn_global_load_lds((const void*)(page + base + off[k]),
+                                         (MLA_LDS void*)(tile + base + 1024 * k), 16, 0, 0);
+    }
+  }
+};
+
+template <int RT, int RGW, int CGW>
+struct Variant {
+  static constexpr int kRT = RT;                 // 16-row tiles per wave
+  static constexpr int kRows = 16 * RT * RGW;    // rows per workgroup
+  static constexpr int kColsPerWave = kDv / CGW;
+  static constexpr int kCT = kColsPerWave / 16;  // 16-column output tiles per wave
+  static constexpr int kKS = kD / 32;            // 18 k-steps of the score product
+};
+
+template <int RT, int RGW, int CGW>
+__global__ void __launch_bounds__(kThreads, 1)
+    decode_kernel(const DecodeParams prm, const uint16_t* __restrict__ q_ptr,
+                  const uint16_t* __restrict__ kv_ptr, const int32_t* __restrict__ block_table,
+                  const int32_t* __restrict__ seqlens, const int32_t* __restrict__ meta,
+                  const int32_t* __restrict__ splits, uint16_t* __restrict__ out_ptr,
+                  float* __restrict__ lse_ptr, float* __restrict__ o_acc,
+                  float* __restrict__ lse_acc) {
+  using V = Variant<RT, RGW, CGW>;
+  constexpr int CT = V::kCT;
+  constexpr int KS = V::kKS;
+
+  __shared__ __attribute__((aligned(1024))) char tile0_[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) char tile1_[kTileBytes];
+  MLA_LDS char* tile0 = (MLA_LDS char*)tile0_;
+  MLA_LDS char* tile1 = (MLA_LDS char*)tile1_;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int l16 = lane & 15;
+  const int g = lane >> 4;
+  const int wr = wave % RGW;  // row sub-group of this wave
+  const int wc = wave / RGW;  // column group of this wave
+
+  // XCD-aware mapping: workgroups of the same partition (its row groups)
+  // share blockIdx % 8 and so land on the same XCD and read its pages
+  // through the same L2.
+  const int bid = blockIdx.x;
+  const int xcd = bid & 7;
+  const int rr = bid >> 3;
+  const int rg = rr % prm.row_groups;
+  const int part = (rr / prm.row_groups) * 8 + xcd;
+  if (part >= prm.num_parts) return;
+
+  const int32_t* m = meta + part * kMetaInts;
+  const int eb = uni(m[2]), ej = uni(m[3]);
+  Item cur = {uni(m[0]), uni(m[1])};
+  if (!item_before(cur, eb, ej)) return;
+  int split_idx = uni(m[4]);
+
+  const int row_base = rg * V::kRows + wr * 16 * RT;  // first row of this wave
+  const int col_base = wc * V::kColsPerWave;
+
+  // lane-constant LDS offsets
+  // K fragment (A of the score product): token 16*tt + l16, logical chunk
+  // 4*ks + g -> physical ((4 ks + g) ^ (l16 & 7)).  The XOR splits into a
+  // per-lane part and a part depending only on ks parity.
+  const int sw = l16 & 7;
+  const int k_lane = l16 * kRowBytes + 16 * (g ^ (sw & 3));
+  const int k_even = k_lane + ((sw & 4) ? 64 : 0);   // ks even: bit 2 of chunk 0 -> sw bit
+  const int k_odd = k_lane - ((sw & 4) ? 64 : 0);    // ks odd:  bit 2 of chunk 1 -> flipped
+  // V^T fragment (A of the value product) by transposed read: token
+  // 32*qq + 16*h + 4*g + (l16 >> 2), columns 16*ct + 4*(l16 & 3) .. +3,
+  // i.e. chunk 2*ct + ((l16 & 3) >> 1), byte 8*(l16 & 1) inside it.
+  const int vt = 4 * g + (l16 >> 2);  // token within a 16-token block
+  const int vsw = swz(vt);
+  const int ve = (l16 & 3) >> 1;
+  int v_off[4];
+#pragma unroll
+  for (int c4 = 0; c4 < 4; ++c4) {
+    const int chunk = (2 * c4 + ve) ^ vsw;  // low 3 bits of 2*ct + ve, ct % 4 = c4
+    v_off[c4] = vt * kRowBytes + 16 * chunk + 8 * (l16 & 1);
+  }
+
+  bf16x8 qf[RT][KS];
+  f32x4 o[RT][CT];
+  float m_used[RT], l_part[RT];
+  int n_vis[RT];
+  int L = 0;
+
+  const char* kvbase = (const char*)kv_ptr;
+  PageLoader loader;
+  loader.init(lane);
+
+  auto begin_segment = [&](int b) __attribute__((always_inline)) {
+    L = uni(seqlens[b]);
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      const int row = row_base + 16 * rt + l16;
+      const bool live = row < prm.R;
+      // rows past R read row 0 and are never stored; they see no tokens, so
+      // their weights are exactly 0
+      const uint16_t* qrow = q_ptr + ((size_t)b * prm.R + (live ? row : 0)) * kD + 8 * g;
+      static_for<0, KS>([&](auto kc) __attribute__((always_inline)) {
+        constexpr int ks = decltype(kc)::value;
+        qf[rt][ks] = *(const bf16x8*)(qrow + 32 * ks);
+      });
+      const int i = (live ? row : 0) / prm.h_q;
+      int n = prm.causal ? (L - prm.s_q + 1 + i) : L;
+      n = n < 0 ? 0 : (n > L ? L : n);
+      n_vis[rt] = live ? n : 0;
+      m_used[rt] = -INFINITY;
+      l_part[rt] = 0.f;
+      static_for<0, CT>([&](auto c) __attribute__((always_inline)) { o[rt][decltype(c)::value] = f32x4{0.f, 0.f, 0.f, 0.f}; });
+    }
+  };
+
+  // Start the copy of item `it`'s page; false if it has no tokens.
+  auto load_item = [&](MLA_LDS char* tile, Item it) __attribute__((always_inline)) -> bool {
+    const int L_it = uni(seqlens[it.b]);
+    if (it.j * kPage >= L_it) return false;
+    const int phys = uni(block_table[(size_t)it.b * prm.max_pages + it.j]);
+    loader.issue(tile, kvbase + (size_t)phys * kTileBytes, wave);
+    return true;
+  };
+
+  auto advance = [&](Item it) __attribute__((always_inline)) {
+    Item nx = it;
+    if (it.j + 1 < page_slots(seqlens, it.b)) {
+      nx.j = uni(it.j + 1);
+    } else {
+      nx.b = uni(it.b + 1);
+      nx.j = 0;
+    }
+    return nx;
+  };
+
+  // One 32-token half of a page: scores, online softmax, value product.
+  auto compute_half = [&](MLA_LDS char* tile, int j, int h) __attribute__((always_inline)) {
+    // ---- scores S^T = K Q^T for tokens 32h .. 32h+31 (token tiles 2h, 2h+1)
+    f32x4 s[RT][2];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) s[rt][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    auto load_k = [&](bf16x8* kf, int ks) __attribute__((always_inline)) {
+      const int base = ((ks & 1) ? k_odd : k_even) + 64 * ks + h * 32 * kRowBytes;
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+        kf[tt] = *(MLA_LDS bf16x8*)(tile + base + tt * 16 * kRowBytes);
+    };
+    auto mma_k = [&](const bf16x8* kf, int ks) __attribute__((always_inline)) {
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+          s[rt][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[tt], qf[rt][ks], s[rt][tt], 0, 0, 0);
+    };
+    bf16x8 kA[2], kB[2];
+    load_k(kA, 0);
+    static_for<0, KS, 2>([&](auto ksc) __attribute__((always_inline)) {
+      constexpr int ks = decltype(ksc)::value;
+      load_k(kB, ks + 1);
+      mma_k(kA, ks);
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (ks + 2 < KS) load_k(kA, ks + 2);
+      mma_k(kB, ks + 1);
+      __builtin_amdgcn_sched_barrier(0);
+    });
+    // ---- online softmax (log2 domain); lane holds row l16, tokens
+    //      32h + 16tt + 4g + r
+    const int tok0 = j * kPage + 32 * h + 4 * g;
+    float rowmax[RT];
+    bool need = false;
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int tok = tok0 + 16 * tt + r;
+          float x = s[rt][tt][r] * prm.scale_log2;
+          x = (tok < n_vis[rt]) ? x : -INFINITY;
+          s[rt][tt][r] = x;
+          mx = fmaxf(mx, x);
+        }
+      mx = wave_max_x4(mx);
+      rowmax[rt] = mx;
+      need |= mx > m_used[rt] + kRescaleThreshold;
+    }
+    if (__builtin_amdgcn_ballot_w64(need) != 0) {
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) {
+        const float mn = fmaxf(m_used[rt], rowmax[rt]);
+        const float alpha = (mn == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_used[rt] - mn);
+        m_used[rt] = mn;
+        l_part[rt] *= alpha;
+        static_for<0, CT>([&](auto c) __attribute__((always_inline)) { o[rt][decltype(c)::value] *= alpha; });
+      }
+    }
+    // weights as the B operand of the value product: k-slot 8g + i is token
+    // 32h + 4g + i (i < 4) or 32h + 16 + 4g + (i - 4)
+    bf16x8 pf[RT];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      const float mref = (m_used[rt] == -INFINITY) ? 0.f : m_used[rt];
+      float p[2][4];
+      float acc = 0.f;
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          p[tt][r] = __builtin_amdgcn_exp2f(s[rt][tt][r] - mref);
+          acc += p[tt][r];
+        }
+      l_part[rt] += acc;
+      bf16x2 a0 = to_bf16x2(p[0][0], p[0][1]);
+      bf16x2 a1 = to_bf16x2(p[0][2], p[0][3]);
+      bf16x2 a2 = to_bf16x2(p[1][0], p[1][1]);
+      bf16x2 a3 = to_bf16x2(p[1][2], p[1][3]);
+      pf[rt] = bf16x8{a0[0], a0[1], a1[0], a1[1], a2[0], a2[1], a3[0], a3[1]};
+    }
+    // ---- O^T += V^T P^T over the same 32 tokens
+    auto load_v = [&](bf16x8& vf, int ct) __attribute__((always_inline)) {
+      const int cta = col_base / 16 + ct;  // absolute 16-column tile
+      const int a = v_off[cta & 3] + 128 * (cta >> 2) + h * 32 * kRowBytes;
+      i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MLA_LDS i16x4*)(tile + a));
+      i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MLA_LDS i16x4*)(tile + a + 16 * kRowBytes));
+      vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    };
+    auto mma_v = [&](const bf16x8& vf, int ct) __attribute__((always_inline)) {
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt)
+        o[rt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[rt], o[rt][ct], 0, 0, 0);
+    };
+    bf16x8 vA, vB;
+    load_v(vA, 0);
+    static_for<0, CT, 2>([&](auto ctc) __attribute__((always_inline)) {
+      constexpr int ct = decltype(ctc)::value;
+      load_v(vB, ct + 1);
+      mma_v(vA, ct);
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (ct + 2 < CT) load_v(vA, ct + 2);
+      mma_v(vB, ct + 1);
+      __builtin_amdgcn_sched_barrier(0);
+    });
+  };
+
+  auto compute_page = [&](MLA_LDS char* tile, int j) __attribute__((always_inline)) {
+    compute_half(tile, j, 0);
+    compute_half(tile, j, 1);
+  };
+
+  auto zero_tail = [&](MLA_LDS char* tile, int first_dead) __attribute__((always_inline)) {
+    // tokens first_dead..63 of the tile may hold anything (a real allocator
+    // does not clear pages); zero them so 0-weight x garbage cannot give NaN
+    const int start = first_dead * kRowBytes;
+    for (int off = start + threadIdx.x * 16; off < kTileBytes; off += kThreads * 16)
+      *(MLA_LDS i32x4*)(tile + off) = i32x4{0, 0, 0, 0};
+  };
+
+  auto finish_segment = [&](int b) __attribute__((always_inline)) {
+    const int s_lo = uni(splits[b]);
+    const int nsplit = uni(splits[b + 1]) - s_lo;
+    const bool direct = nsplit <= 1;
+    const int slot = s_lo + split_idx;
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      const int row = row_base + 16 * rt + l16;
+      const float lt = wave_sum_x4(l_part[rt]);
+      const float inv = lt > 0.f ? 1.f / lt : 0.f;
+      const float lse2 = lt > 0.f ? m_used[rt] + __builtin_amdgcn_logf(lt) : -INFINITY;
+      if (row < prm.R) {
+        if (direct) {
+          uint16_t* orow = out_ptr + ((size_t)b * prm.R + row) * kDv + col_base + 4 * g;
+          static_for<0, CT>([&](auto cc) __attribute__((always_inline)) {
+            constexpr int ct = decltype(cc)::value;
+            f32x4 v = o[rt][ct] * inv;
+            bf16x2 a = to_bf16x2(v[0], v[1]);
+            bf16x2 c = to_bf16x2(v[2], v[3]);
+            bf16x4 w = {a[0], a[1], c[0], c[1]};
+            *(bf16x4*)(orow + 16 * ct) = w;
+          });
+          if (g == 0 && wc == 0) lse_ptr[(size_t)b * prm.R + row] = lse2 * kLn2;
+        } else {
+          float* orow = o_acc + ((size_t)slot * prm.R + row) * kDv + col_base + 4 * g;
+          static_for<0, CT>([&](auto cc) __attribute__((always_inline)) {
+            constexpr int ct = decltype(cc)::value;
+            *(f32x4*)(orow + 16 * ct) = o[rt][ct] * inv;
+          });
+          if (g == 0 && wc == 0) lse_acc[(size_t)slot * prm.R + row] = lse2;
+        }
+      }
+    }
+    split_idx = 0;  // later sequences of this partition start at their page 0
+  };
+
+  // One step: compute `cur` from tile A while the next item streams into B.
+  // The query fragments of a sequence are loaded at the end of the step
+  // before its first page, so the wait at the top of the step (needed for
+  // the page anyway) also covers them and no load into registers is ever
+  // pending next to a page copy.
+  auto step = [&](MLA_LDS char* tA, MLA_LDS char* tB) __attribute__((always_inline)) -> bool {
+    const Item nx = advance(cur);
+    const bool has_next = item_before(nx, eb, ej);
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);  // this wave's part of tile A landed
+    __syncthreads();                       // ... and every wave's; B is free
+    if (has_next) load_item(tB, nx);
+    const bool has_tokens = cur.j * kPage < L;
+    if (has_tokens) {
+      const int live = L - cur.j * kPage;
+      if (live < kPage) {
+        zero_tail(tA, live);
+        lds_barrier();
+      }
+      compute_page(tA, cur.j);
+    }
+    if (!has_next || nx.b != cur.b) {
+      finish_segment(cur.b);
+      if (has_next) begin_segment(nx.b);
+    }
+    cur = nx;
+    return has_next;
+  };
+
+  begin_segment(cur.b);
+  load_item(tile0, cur);
+  while (true) {
+    if (!step(tile0, tile1)) break;
+    if (!step(tile1, tile0)) break;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Combine: merge split partials by log-sum-exp.  One 64-thread slice per
+// query row, 8 output columns per thread; four rows per workgroup.
+__global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ o_acc,
+                                                      const float* __restrict__ lse_acc,
+                                                      const int32_t* __restrict__ splits, int R,
+                                                      uint16_t* __restrict__ out,
+                                                      float* __restrict__ lse) {
+  const int b = blockIdx.y;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int t = threadIdx.x & 63;
+  const int s0 = splits[b];
+  const int ns = splits[b + 1] - s0;
+  if (ns <= 1 || row >= R) return;
+  float mx = -INFINITY;
+  for (int s = 0; s < ns; ++s) mx = fmaxf(mx, lse_acc[(size_t)(s0 + s) * R + row]);
+  uint16_t* orow = out + ((size_t)b * R + row) * kDv + 8 * t;
+  if (mx == -INFINITY) {
+    *(i32x4*)orow = i32x4{0, 0, 0, 0};
+    if (t == 0) lse[(size_t)b * R + row] = -INFINITY;
+    return;
+  }
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  float z = 0.f;
+  for (int s = 0; s < ns; ++s) {
+    const float ls = lse_acc[(size_t)(s0 + s) * R + row];
+    const float w = __builtin_amdgcn_exp2f(ls - mx);  // -inf -> 0
+    z += w;
+    const float* src = o_acc + ((size_t)(s0 + s) * R + row) * kDv + 8 * t;
+    const f32x4 a = *(const f32x4*)src;
+    const f32x4 c = *(const f32x4*)(src + 4);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      acc[k] += w * a[k];
+      acc[4 + k] += w * c[k];
+    }
+  }
+  const float inv = 1.f / z;
+  bf16x2 r0 = to_bf16x2(acc[0] * inv, acc[1] * inv);
+  bf16x2 r1 = to_bf16x2(acc[2] * inv, acc[3] * inv);
+  bf16x2 r2 = to_bf16x2(acc[4] * inv, acc[5] * inv);
+  bf16x2 r3 = to_bf16x2(acc[6] * inv, acc[7] * inv);
+  *(bf16x8*)orow = bf16x8{r0[0], r0[1], r1[0], r1[1], r2[0], r2[1], r3[0], r3[1]};
+  if (t == 0) lse[(size_t)b * R + row] = (mx + __builtin_amdgcn_logf(z)) * kLn2;
+}
+
+}  // namespace mla
+
+// ---------------------------------------------------------------------------
+// launchers (called by the C ABI after argument checks)
+extern "C" hipError_t mla_launch_decode(const mla::DecodeParams* prm, int rows_variant,
+                                        hipStream_t stream) {
+  using namespace mla;
+  const int groups = (prm->num_parts + 7) / 8;
+  const dim3 grid(groups * 8 * prm->row_groups);
+  const dim3 block(kThreads);
+#define MLA_DECODE_ARGS                                                                  \
+  *prm, prm->q, prm->kv, prm->block_table, prm->seqlens, prm->meta, prm->splits, prm->out, \
+      prm->lse, prm->o_acc, prm->lse_acc
+  switch (rows_variant) {
+    case 16:
+      hipLaunchKernelGGL((decode_kernel<1, 1, 4>), grid, block, 0, stream, MLA_DECODE_ARGS);
+      break;
+    case 32:
+      hipLaunchKernelGGL((decode_kernel<1, 2, 2>), grid, block, 0, stream, MLA_DECODE_ARGS);
+      break;
+    case 64:
+      hipLaunchKernelGGL((decode_kernel<1, 4, 1>), grid, block, 0, stream, MLA_DECODE_ARGS);
+      break;
+    default:
+      return hipErrorInvalidValue;
+  }
+#undef MLA_DECODE_ARGS
+  return hipGetLastError();
+}
+
+extern "C" hipError_t mla_launch_combine(const float* o_acc, const float* lse_acc,
+                                         const int32_t* splits, int batch, int R, uint16_t* out,
+                                         float* lse, hipStream_t stream) {
+  const dim3 grid((R + 3) / 4, batch);
+  hipLaunchKernelGGL(mla::combine_kernel, grid, dim3(256), 0, stream, o_acc, lse_acc, splits, R,
+                     out, lse);
+  return hipGetLastError();
+}

@@ -1,0 +1,110 @@
+"""The C-ABI library builds, loads and exports what include/mla_paged.h declares.
+
+Host-only calls: no GPU is needed (argument checks fail before any HIP call).
+"""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mla_paged.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import mla_paged_kv_06_amd as m
+    if not os.path.exists(m.library_path()):
+        from mla_paged_kv_06_amd import build
+        build.build()
+    return m.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^[A-Za-z_][\w\s\*]*?\b(mla_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_three_calls():
+    names = declared_functions()
+    for f in ("mla_get_metadata", "mla_decode_paged", "mla_combine"):
+        assert f in names
+    assert len(names) >= 7
+
+
+def test_every_declared_symbol_is_exported(lib):
+    import mla_paged_kv_06_amd as m
+    out = subprocess.run(["nm", "-D", "--defined-only", m.library_path()],
+                         capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r"\sT\s+(\w+)$", out, flags=re.M))
+    for name in declared_functions():
+        assert name in exported, name
+        assert getattr(lib, name) is not None
+
+
+def test_header_compiles_as_c():
+    # the header is self-contained C
+    src = '#include "mla_paged.h"\nint main(void){return MLA_OK;}\n'
+    res = subprocess.run(["gcc", "-x", "c", "-std=c99", "-fsyntax-only",
+                          "-I", os.path.join(ROOT, "include"),
+                          "-I", "/opt/rocm/include", "-D__HIP_PLATFORM_AMD__", "-"],
+                         input=src, capture_output=True, text=True)
+    assert res.returncode == 0, res.stderr
+
+
+def test_status_strings(lib):
+    for code, text in [(0, "ok"), (1, "invalid argument"), (2, "unsupported shape"),
+                       (3, "workspace too small"), (4, "HIP runtime error")]:
+        assert lib.mla_status_string(code).decode() == text
+
+
+def test_partitions_and_sizes(lib):
+    # at most 64 query rows per workgroup; partitions x row groups ~ CUs
+    assert lib.mla_num_partitions(1, 16, 256) == 256
+    assert lib.mla_num_partitions(1, 64, 256) == 256
+    assert lib.mla_num_partitions(1, 128, 256) == 128
+    assert lib.mla_num_partitions(2, 128, 256) == 64
+    assert lib.mla_num_partitions(1, 16, 1) == 1
+    assert lib.mla_num_partitions(2, 128, 3) == 1
+    assert lib.mla_num_partitions(0, 16, 256) == 0
+    assert lib.mla_num_partitions(1, 4096, 256) == 0  # more rows than supported
+    assert lib.mla_metadata_ints(1, 16, 256) == 256 * 8
+    R = 16
+    ws = lib.mla_workspace_bytes(8, 1, 16, 256)
+    need = (8 + 256) * R * 512 * 4 + (8 + 256) * R * 4
+    assert need <= ws <= need + 512
+    assert lib.mla_workspace_bytes(0, 1, 16, 256) == 0
+
+
+def test_invalid_arguments_launch_nothing(lib):
+    null = ctypes.c_void_p(0)
+    one = ctypes.c_void_p(16)
+    assert lib.mla_get_metadata(null, 4, 1, 16, 8, one, one, null) == 1
+    assert lib.mla_get_metadata(one, 0, 1, 16, 8, one, one, null) == 1
+    assert lib.mla_get_metadata(one, 4, 1, 4096, 8, one, one, null) == 2
+    args = [one, one, one, one, 4, 1, 16, 10, 4, 0.1, 0, one, one, 8, one, 10 ** 9, one, one, null]
+    bad = list(args); bad[0] = null
+    assert lib.mla_decode_paged(*bad) == 1
+    bad = list(args); bad[9] = float("nan")
+    assert lib.mla_decode_paged(*bad) == 1
+    bad = list(args); bad[7] = 0  # num_pages
+    assert lib.mla_decode_paged(*bad) == 1
+    bad = list(args); bad[15] = 100  # workspace too small
+    assert lib.mla_decode_paged(*bad) == 3
+    bad = list(args); bad[0] = ctypes.c_void_p(18)  # misaligned q
+    assert lib.mla_decode_paged(*bad) == 1
+    assert lib.mla_combine(null, 10 ** 9, one, 4, 1, 16, 8, one, one, null) == 1
+    assert lib.mla_combine(one, 10, one, 4, 1, 16, 8, one, one, null) == 3
+
+
+def test_product_path_does_not_import_the_oracle():
+    pkg = os.path.join(ROOT, "mla_paged_kv_06_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".h", ".cpp")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert "oracle" not in text.replace("oracle_", ""), f

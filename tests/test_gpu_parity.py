@@ -1,0 +1,202 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 CPU oracle.
+
+Gates: every output element within 1e-2 absolute plus 2e-2 relative
+(|g - r| <= 1e-2 + 2e-2 |r|, the allclose form of the stated tolerance), the
+normwise relative error of ``out`` at most 2e-2, and ``lse`` within 1e-3
+absolute; empty rows must give exactly out = 0 and lse = -inf on both sides.
+The output is bf16: for |out| in [2, 4) one bf16 ulp is 2^-6, so rounding
+alone may cost 7.8e-3, which is why the relative term is needed.
+"""
+
+import math
+import os
+import sys
+
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+import oracle  # noqa: E402
+from workloads import make_case, make_config_case  # noqa: E402
+from casebuild import permute_pool  # noqa: E402
+from sched_model import schedule  # noqa: E402
+
+OUT_ATOL = 1e-2
+OUT_RTOL = 2e-2
+OUT_NORM_RTOL = 2e-2
+LSE_ATOL = 1e-3
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def mla():
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible to torch")
+    import mla_paged_kv_06_amd as m
+    m.load_library()  # raises if the HIP library is missing
+    return m
+
+
+def to_dev(case):
+    dev = torch.device("cuda:0")
+    q = torch.from_numpy(case.q.view(np.int16)).to(dev).view(torch.bfloat16)
+    kv = torch.from_numpy(case.kv.view(np.int16)).to(dev).view(torch.bfloat16)
+    bt = torch.from_numpy(case.block_table).to(dev)
+    sl = torch.from_numpy(case.cache_seqlens).to(dev)
+    return q, kv, bt, sl
+
+
+def run(mla, case, num_cus=0):
+    q, kv, bt, sl = to_dev(case)
+    out, lse = mla.mla_decode(q, kv, bt, sl, case.softmax_scale, case.causal, num_cus=num_cus)
+    torch.cuda.synchronize()
+    o = out.view(torch.int16).cpu().numpy().view(np.uint16)
+    return oracle.bf16_to_f64(o), lse.cpu().numpy().astype(np.float64)
+
+
+def compare(out, lse, ref_out, ref_lse, batches=None):
+    if batches is not None:
+        out, lse = out[batches], lse[batches]
+        ref_out, ref_lse = ref_out[batches], ref_lse[batches]
+    empty = np.isneginf(ref_lse)
+    assert np.array_equal(np.isneginf(lse), empty), "empty rows differ"
+    assert np.all(out[empty] == 0.0)
+    assert np.all(np.isfinite(out)), "non-finite output"
+    live = ~empty
+    if not np.any(live):
+        return 0.0, 0.0, 0.0
+    err = np.abs(out - ref_out)
+    max_abs = float(err.max())
+    excess = float((err - (OUT_ATOL + OUT_RTOL * np.abs(ref_out))).max())
+    nrm = float(np.linalg.norm(out[live] - ref_out[live]) / max(np.linalg.norm(ref_out[live]), 1e-30))
+    lse_err = float(np.abs(lse[live] - ref_lse[live]).max())
+    assert excess <= 0.0, f"out outside atol+rtol*|ref| (max abs err {max_abs})"
+    assert nrm <= OUT_NORM_RTOL, f"out normwise rel err {nrm}"
+    assert lse_err <= LSE_ATOL, f"lse max abs err {lse_err}"
+    return max_abs, nrm, lse_err
+
+
+# ---------------------------------------------------------------- the five workloads
+@pytest.mark.parametrize("k", [1, 2, 3, 5])
+def test_config_full_parity(mla, k):
+    _say(f"[parity] workload {k}: full oracle")
+    case = make_config_case(k, poison_unused=True, poison_tail=True)
+    out, lse = run(mla, case)
+    ref_out, ref_lse = oracle.decode_ref(case)
+    errs = compare(out, lse, ref_out, ref_lse)
+    _say(f"[parity] workload {k}: max|err| {errs[0]:.2e} norm {errs[1]:.2e} lse {errs[2]:.2e}")
+
+
+def test_config4_sampled_parity(mla):
+    _say("[parity] workload 4: sampled batches")
+    case = make_config_case(4)
+    out, lse = run(mla, case)
+    L = case.cache_seqlens
+    pick = sorted({int(np.argmin(L)), int(np.argmax(L)), 0, 63, 127, 5, 77, 101})
+    ref_out, ref_lse = oracle.decode_ref(case, batches=pick)
+    errs = compare(out, lse, ref_out, ref_lse, batches=pick)
+    _say(f"[parity] workload 4 batches {pick}: {errs}")
+
+
+# ---------------------------------------------------------------- edge cases
+EDGE_L = [1, 63, 64, 65, 127, 128, 4097]
+
+
+@pytest.mark.parametrize("h_q", [1, 16, 64, 128])
+@pytest.mark.parametrize("s_q,causal", [(1, False), (2, True), (2, False)])
+def test_edge_lengths(mla, h_q, s_q, causal):
+    _say(f"[parity] edge lengths h_q={h_q} s_q={s_q} causal={causal}")
+    case = make_case(EDGE_L, s_q, h_q, causal, seed=17 + h_q, pool_factor=1.25,
+                     poison_unused=True, poison_tail=True)
+    out, lse = run(mla, case)
+    ref_out, ref_lse = oracle.decode_ref(case)
+    compare(out, lse, ref_out, ref_lse)
+
+
+@pytest.mark.parametrize("num_cus", [1, 3, 64, 256, 1024])
+def test_forced_partition_counts(mla, num_cus):
+    _say(f"[parity] num_cus={num_cus}")
+    case = make_case([1, 200, 4097, 65, 0, 3000], 2, 16, True, seed=23, pool_factor=1.25,
+                     poison_unused=True, poison_tail=True)
+    out, lse = run(mla, case, num_cus=num_cus)
+    ref_out, ref_lse = oracle.decode_ref(case)
+    compare(out, lse, ref_out, ref_lse)
+
+
+def test_empty_and_single_token(mla):
+    _say("[parity] empty / single-token sequences")
+    case = make_case([0, 1, 0, 2], 1, 16, False, seed=29)
+    out, lse = run(mla, case)
+    ref_out, ref_lse = oracle.decode_ref(case)
+    compare(out, lse, ref_out, ref_lse)
+    assert np.all(np.isneginf(lse[0])) and np.all(out[0] == 0)
+
+
+def test_fully_masked_split_partials(mla):
+    """s_q = 2 causal with L = 64k + 1: a split holding only the last token is
+    empty for query 0 (lse_s = -inf) and must carry no weight."""
+    _say("[parity] masked partials")
+    case = make_case([64 * 40 + 1, 64 * 7 + 1], 2, 64, True, seed=31)
+    for num_cus in (64, 256, 1024):
+        out, lse = run(mla, case, num_cus=num_cus)
+        ref_out, ref_lse = oracle.decode_ref(case)
+        compare(out, lse, ref_out, ref_lse)
+
+
+# ---------------------------------------------------------------- properties
+def test_value_all_ones_probe(mla):
+    _say("[parity] V == 1 probe")
+    case = make_case([700, 64, 3], 2, 16, True, seed=37)
+    case.kv[:, :, :512] = np.uint16(0x3F80)
+    out, lse = run(mla, case)
+    assert np.max(np.abs(out - 1.0)) <= OUT_ATOL + OUT_RTOL
+
+
+def test_deterministic_and_page_permutation_invariant(mla):
+    _say("[parity] determinism and page permutation")
+    case = make_case([3000, 129, 64], 1, 64, False, seed=41, pool_factor=1.25)
+    a = run(mla, case)
+    b = run(mla, case)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+    c = run(mla, permute_pool(case, seed=5))
+    assert np.array_equal(a[0], c[0]) and np.array_equal(a[1], c[1])
+
+
+@pytest.mark.parametrize("s_q,h_q,num_cus", [(1, 16, 0), (2, 128, 0), (1, 64, 3), (1, 16, 1024)])
+def test_device_schedule_matches_model(mla, s_q, h_q, num_cus):
+    _say(f"[sched] s_q={s_q} h_q={h_q} num_cus={num_cus}")
+    rng = np.random.Generator(np.random.PCG64(43))
+    L = list(rng.integers(0, 20000, size=37)) + [131072, 0, 1, 64]
+    sl = torch.tensor(L, dtype=torch.int32, device="cuda:0")
+    meta, splits = mla.get_metadata(sl, s_q, h_q, num_cus)
+    torch.cuda.synchronize()
+    meta = meta.cpu().numpy()
+    splits = splits.cpu().numpy()
+    parts = meta.shape[0]
+    c0 = int(meta[0, 6])
+    ref_meta, ref_splits, _ = schedule(L, parts, c0)
+    assert np.array_equal(meta, np.array(ref_meta, dtype=np.int32))
+    assert np.array_equal(splits, np.array(ref_splits, dtype=np.int32))
+
+
+def test_error_codes(mla):
+    q = torch.zeros((2, 1, 16, 576), dtype=torch.bfloat16, device="cuda:0")
+    kv = torch.zeros((4, 64, 576), dtype=torch.bfloat16, device="cuda:0")
+    bt = torch.zeros((2, 2), dtype=torch.int32, device="cuda:0")
+    sl = torch.full((2,), 64, dtype=torch.int32, device="cuda:0")
+    meta, splits = mla.get_metadata(sl, 1, 16)
+    with pytest.raises(mla.MlaError):
+        mla.decode_paged(q, kv, bt, sl, float("inf"), False, meta, splits)
+    small = torch.empty((64,), dtype=torch.uint8, device="cuda:0")
+    with pytest.raises(mla.MlaError) as e:
+        mla.decode_paged(q, kv, bt, sl, 0.1, False, meta, splits, workspace=small)
+    assert e.value.status == 3
+    with pytest.raises(TypeError):
+        mla.decode_paged(q.float(), kv, bt, sl, 0.1, False, meta, splits)
