@@ -76,6 +76,7 @@ size_t ws_bytes(int batch, int R, int parts) {
 
 extern "C" hipError_t mla_launch_decode(const mla::DecodeParams* prm, int rows_variant,
                                         hipStream_t stream);
+extern "C" hipError_t mla_launch_decode_split(const mla::DecodeParams* prm, hipStream_t stream);
 extern "C" hipError_t mla_launch_combine(const float* o_acc, const float* lse_acc,
                                          const int32_t* splits, int batch, int R, uint16_t* out,
                                          float* lse, hipStream_t stream);
@@ -150,7 +151,9 @@ mla_status_t mla_decode_paged(const void* q, const void* kv_cache, const int32_t
   prm.row_groups = row_groups_of(R);
   prm.causal = causal ? 1 : 0;
   prm.scale_log2 = (float)((double)softmax_scale * 1.4426950408889634);
-  hipError_t e = mla_launch_decode(&prm, rows_variant_of(R), stream);
+  const int variant = rows_variant_of(R);
+  hipError_t e = variant == 64 ? mla_launch_decode_split(&prm, stream)
+                               : mla_launch_decode(&prm, variant, stream);
   return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 

@@ -29,70 +29,19 @@
 //     first 512 values of the latent) and the bf16 weights as B.  Each lane
 //     again holds one query row, so the rescale of O is a per-lane scalar.
 //
-// Variants (query rows per workgroup; wave grid rows x cols):
-//   16 rows: 1 x 4 waves, each wave all 16 rows and 128 output columns
-//            (the score product is repeated per wave; it is cheap here);
-//   32 rows: 2 x 2;  64 rows: 4 x 1;  128 rows: 4 x 1 with 32 rows per wave.
+// Variants (query rows per workgroup; waves as row groups x column groups):
+//   16 rows: 1 x 4, each wave all 16 rows and 128 output columns;
+//   32 rows: 1 x 4, each wave all 32 rows (two 16-row tiles) and 128 columns;
+//   64 rows: 2 x 2, each wave 32 rows and 256 columns.
+// Waves of one row group repeat its score product (cheap next to the LDS
+// traffic it saves): every K fragment read serves 32 rows, and each wave
+// reads only its columns of V^T, whose transposed reads are the slowest LDS
+// access on gfx950 (about 85 B/clk per CU against 200 B/clk for ds_read_b128).
 
-#include "mla_device.h"
+#include "mla_decode_common.h"
 
 namespace mla {
 
-
-struct Item {
-  int b, j;
-};
-
-__device__ __forceinline__ bool item_before(Item a, int eb, int ej) {
-  return a.b < eb || (a.b == eb && a.j < ej);
-}
-
-// Wave-uniform value (kept in an SGPR, so loads indexed by it are scalar).
-__device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
-
-// Barrier for LDS traffic only: unlike __syncthreads it does not wait for
-// outstanding global loads, so a page prefetch in flight keeps flying.
-__device__ __forceinline__ void lds_barrier() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
-__device__ __forceinline__ int page_slots(const int32_t* seqlens, int b) {
-  int L = uni(seqlens[b]);
-  int n = (L + kPage - 1) / kPage;
-  return n > 0 ? n : 1;
-}
-
-// Copy one 64-token page into an LDS tile.  The page is 8 blocks of 8 tokens
-// (9216 B each = 9 wave-wide 1 KiB loads); wave w copies blocks 2w and 2w+1.
-// Inside a block, load k, lane l fills LDS chunk 64 k + l of the block:
-// token t' = (64 k + l) / 72, physical chunk p = (64 k + l) % 72, which
-// holds logical chunk p ^ swz(t').  swz depends on t & 7 only, so the nine
-// per-lane source offsets are the same for every block.
-struct PageLoader {
-  int off[9];  // per-lane source byte offsets inside an 8-token block
-  __device__ __forceinline__ void init(int lane) {
-#pragma unroll
-    for (int k = 0; k < 9; ++k) {
-      const int pc = 64 * k + lane;
-      const int t = pc / kChunksPerRow;
-      const int p = pc - t * kChunksPerRow;
-      off[k] = t * kRowBytes + 16 * (p ^ swz(t));
-    }
-  }
-  __device__ __forceinline__ void issue(MLA_LDS char* tile, const char* page, int wave) const {
-#pragma unroll
-    for (int blk = 0; blk < 2; ++blk) {
-      const int base = (2 * wave + blk) * 8 * kRowBytes;  // == 9 KiB of LDS per block
-#pragma unroll
-      for (int k = 0; k < 9; ++k)
-        __builtin_amdgcn_global_load_lds((const void*)(page + base + off[k]),
-                                         (MLA_LDS void*)(tile + base + 1024 * k), 16, 0, 0);
-    }
-  }
-};
 
 template <int RT, int RGW, int CGW>
 struct Variant {
@@ -121,7 +70,7 @@ __global__ void __launch_bounds__(kThreads, 1)
   MLA_LDS char* tile1 = (MLA_LDS char*)tile1_;
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = uni(threadIdx.x >> 6);  // wave-uniform: SGPR offsets and M0
   const int l16 = lane & 15;
   const int g = lane >> 4;
   const int wr = wave % RGW;  // row sub-group of this wave
@@ -209,6 +158,23 @@ __global__ void __launch_bounds__(kThreads, 1)
     return true;
   };
 
+  // The copy of the next item's page, to be issued during the score product.
+  auto next_copy = [&](MLA_LDS char* tile, Item it, bool has) __attribute__((always_inline)) {
+    PendingCopy cp;
+    cp.tile = tile;
+    cp.valid = false;
+    cp.rsrc = PageLoader::resource(kvbase);
+    if (has) {
+      const int L_it = uni(seqlens[it.b]);
+      if (it.j * kPage < L_it) {
+        const int phys = uni(block_table[(size_t)it.b * prm.max_pages + it.j]);
+        cp.rsrc = PageLoader::resource(kvbase + (size_t)phys * kTileBytes);
+        cp.valid = true;
+      }
+    }
+    return cp;
+  };
+
   auto advance = [&](Item it) __attribute__((always_inline)) {
     Item nx = it;
     if (it.j + 1 < page_slots(seqlens, it.b)) {
@@ -221,7 +187,9 @@ __global__ void __launch_bounds__(kThreads, 1)
   };
 
   // One 32-token half of a page: scores, online softmax, value product.
-  auto compute_half = [&](MLA_LDS char* tile, int j, int h) __attribute__((always_inline)) {
+  auto compute_half = [&](MLA_LDS char* tile, int j, auto hc, const PendingCopy& cp)
+                          __attribute__((always_inline)) {
+    constexpr int h = decltype(hc)::value;
     // ---- scores S^T = K Q^T for tokens 32h .. 32h+31 (token tiles 2h, 2h+1)
     f32x4 s[RT][2];
 #pragma unroll
@@ -241,16 +209,35 @@ __global__ void __launch_bounds__(kThreads, 1)
         for (int tt = 0; tt < 2; ++tt)
           s[rt][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[tt], qf[rt][ks], s[rt][tt], 0, 0, 0);
     };
-    bf16x8 kA[2], kB[2];
-    load_k(kA, 0);
-    static_for<0, KS, 2>([&](auto ksc) __attribute__((always_inline)) {
+    auto load_v = [&](bf16x8& vf, int ct) __attribute__((always_inline)) {
+      const int cta = col_base / 16 + ct;  // absolute 16-column tile
+      const int a = v_off[cta & 3] + 128 * (cta >> 2) + h * 32 * kRowBytes;
+      i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MLA_LDS i16x4*)(tile + a));
+      i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MLA_LDS i16x4*)(tile + a + 16 * kRowBytes));
+      vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    };
+    // K fragments run DK k-steps ahead of the products that use them: with
+    // one wave per SIMD nothing else hides the LDS latency.
+    constexpr int DK = RT == 1 ? 6 : 2;
+    bf16x8 kr[DK + 1][2];
+    static_for<0, DK>([&](auto ic) __attribute__((always_inline)) {
+      load_k(kr[decltype(ic)::value], decltype(ic)::value);
+    });
+    static_for<0, KS>([&](auto ksc) __attribute__((always_inline)) {
       constexpr int ks = decltype(ksc)::value;
-      load_k(kB, ks + 1);
-      mma_k(kA, ks);
+      if constexpr (ks + DK < KS) load_k(kr[(ks + DK) % (DK + 1)], ks + DK);
+      if constexpr (h == 0) {
+        static_assert(KS == kLoadsPerWave, "one page-copy instruction per k-step");
+        if (cp.valid) loader.issue_one(cp.tile, cp.rsrc, wave, ks);
+      }
+      mma_k(kr[ks % (DK + 1)], ks);
       __builtin_amdgcn_sched_barrier(0);
-      if constexpr (ks + 2 < KS) load_k(kA, ks + 2);
-      mma_k(kB, ks + 1);
-      __builtin_amdgcn_sched_barrier(0);
+    });
+    // the first V^T fragments are independent of the weights: start them now
+    constexpr int DV = RT == 1 ? 4 : 3;
+    bf16x8 vr[DV + 1];
+    static_for<0, DV>([&](auto ic) __attribute__((always_inline)) {
+      load_v(vr[decltype(ic)::value], decltype(ic)::value);
     });
     // ---- online softmax (log2 domain); lane holds row l16, tokens
     //      32h + 16tt + 4g + r
@@ -307,34 +294,23 @@ __global__ void __launch_bounds__(kThreads, 1)
       pf[rt] = bf16x8{a0[0], a0[1], a1[0], a1[1], a2[0], a2[1], a3[0], a3[1]};
     }
     // ---- O^T += V^T P^T over the same 32 tokens
-    auto load_v = [&](bf16x8& vf, int ct) __attribute__((always_inline)) {
-      const int cta = col_base / 16 + ct;  // absolute 16-column tile
-      const int a = v_off[cta & 3] + 128 * (cta >> 2) + h * 32 * kRowBytes;
-      i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MLA_LDS i16x4*)(tile + a));
-      i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MLA_LDS i16x4*)(tile + a + 16 * kRowBytes));
-      vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-    };
     auto mma_v = [&](const bf16x8& vf, int ct) __attribute__((always_inline)) {
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt)
         o[rt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[rt], o[rt][ct], 0, 0, 0);
     };
-    bf16x8 vA, vB;
-    load_v(vA, 0);
-    static_for<0, CT, 2>([&](auto ctc) __attribute__((always_inline)) {
+    static_for<0, CT>([&](auto ctc) __attribute__((always_inline)) {
       constexpr int ct = decltype(ctc)::value;
-      load_v(vB, ct + 1);
-      mma_v(vA, ct);
-      __builtin_amdgcn_sched_barrier(0);
-      if constexpr (ct + 2 < CT) load_v(vA, ct + 2);
-      mma_v(vB, ct + 1);
+      if constexpr (ct + DV < CT) load_v(vr[(ct + DV) % (DV + 1)], ct + DV);
+      mma_v(vr[ct % (DV + 1)], ct);
       __builtin_amdgcn_sched_barrier(0);
     });
   };
 
-  auto compute_page = [&](MLA_LDS char* tile, int j) __attribute__((always_inline)) {
-    compute_half(tile, j, 0);
-    compute_half(tile, j, 1);
+  auto compute_page = [&](MLA_LDS char* tile, int j, const PendingCopy& cp)
+                          __attribute__((always_inline)) {
+    compute_half(tile, j, std::integral_constant<int, 0>{}, cp);
+    compute_half(tile, j, std::integral_constant<int, 1>{}, cp);
   };
 
   auto zero_tail = [&](MLA_LDS char* tile, int first_dead) __attribute__((always_inline)) {
@@ -391,7 +367,7 @@ __global__ void __launch_bounds__(kThreads, 1)
     const bool has_next = item_before(nx, eb, ej);
     __builtin_amdgcn_s_waitcnt(kWaitVm0);  // this wave's part of tile A landed
     __syncthreads();                       // ... and every wave's; B is free
-    if (has_next) load_item(tB, nx);
+    PendingCopy cp = next_copy(tB, nx, has_next);
     const bool has_tokens = cur.j * kPage < L;
     if (has_tokens) {
       const int live = L - cur.j * kPage;
@@ -399,7 +375,9 @@ __global__ void __launch_bounds__(kThreads, 1)
         zero_tail(tA, live);
         lds_barrier();
       }
-      compute_page(tA, cur.j);
+      compute_page(tA, cur.j, cp);
+    } else if (cp.valid) {
+      for (int i = 0; i < kLoadsPerWave; ++i) loader.issue_one(cp.tile, cp.rsrc, wave, i);
     }
     if (!has_next || nx.b != cur.b) {
       finish_segment(cur.b);
@@ -418,47 +396,82 @@ __global__ void __launch_bounds__(kThreads, 1)
 }
 
 // ---------------------------------------------------------------------------
-// Combine: merge split partials by log-sum-exp.  One 64-thread slice per
-// query row, 8 output columns per thread; four rows per workgroup.
+// Combine: merge split partials by log-sum-exp.  One wave per query row
+// (4 rows per workgroup), 8 output columns per lane.  The weights of all
+// splits are computed first (lanes over splits, a wave max and sum), kept in
+// LDS, and the partial rows are then read with several loads in flight.
+constexpr int kCombineRows = 4;
+constexpr int kCombineChunk = 1024;  // splits whose weights sit in LDS at once
+
 __global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ o_acc,
                                                       const float* __restrict__ lse_acc,
                                                       const int32_t* __restrict__ splits, int R,
                                                       uint16_t* __restrict__ out,
                                                       float* __restrict__ lse) {
+  __shared__ float s_w[kCombineRows][kCombineChunk];
   const int b = blockIdx.y;
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int wv = threadIdx.x >> 6;
+  const int row = blockIdx.x * kCombineRows + wv;
   const int t = threadIdx.x & 63;
   const int s0 = splits[b];
   const int ns = splits[b + 1] - s0;
-  if (ns <= 1 || row >= R) return;
-  float mx = -INFINITY;
-  for (int s = 0; s < ns; ++s) mx = fmaxf(mx, lse_acc[(size_t)(s0 + s) * R + row]);
+  if (ns <= 1 || row >= R) return;  // uniform per wave; no block barrier below
+  const float* lrow = lse_acc + (size_t)s0 * R + row;
+  // the first 64 splits' lse sit in one register per lane (one load round)
+  const float l0 = t < ns ? lrow[(size_t)t * R] : -INFINITY;
+  float mx = l0;
+  for (int s = t + 64; s < ns; s += 64) mx = fmaxf(mx, lrow[(size_t)s * R]);
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) mx = fmaxf(mx, __shfl_xor(mx, d));
   uint16_t* orow = out + ((size_t)b * R + row) * kDv + 8 * t;
   if (mx == -INFINITY) {
     *(i32x4*)orow = i32x4{0, 0, 0, 0};
     if (t == 0) lse[(size_t)b * R + row] = -INFINITY;
     return;
   }
-  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  float z = 0.f;
-  for (int s = 0; s < ns; ++s) {
-    const float ls = lse_acc[(size_t)(s0 + s) * R + row];
-    const float w = __builtin_amdgcn_exp2f(ls - mx);  // -inf -> 0
-    z += w;
-    const float* src = o_acc + ((size_t)(s0 + s) * R + row) * kDv + 8 * t;
-    const f32x4 a = *(const f32x4*)src;
-    const f32x4 c = *(const f32x4*)(src + 4);
+  const float w0 = __builtin_amdgcn_exp2f(l0 - mx);  // -inf -> 0
+  float z = w0;
+  for (int s = t + 64; s < ns; s += 64) z += __builtin_amdgcn_exp2f(lrow[(size_t)s * R] - mx);
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      acc[k] += w * a[k];
-      acc[4 + k] += w * c[k];
-    }
-  }
+  for (int d = 32; d >= 1; d >>= 1) z += __shfl_xor(z, d);
   const float inv = 1.f / z;
-  bf16x2 r0 = to_bf16x2(acc[0] * inv, acc[1] * inv);
-  bf16x2 r1 = to_bf16x2(acc[2] * inv, acc[3] * inv);
-  bf16x2 r2 = to_bf16x2(acc[4] * inv, acc[5] * inv);
-  bf16x2 r3 = to_bf16x2(acc[6] * inv, acc[7] * inv);
+  f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0;
+  const float* orow_acc = o_acc + ((size_t)s0 * R + row) * kDv + 8 * t;
+  constexpr int U = 8;  // partial rows in flight per lane
+  for (int c0 = 0; c0 < ns; c0 += kCombineChunk) {
+    const int nc = ns - c0 < kCombineChunk ? ns - c0 : kCombineChunk;
+    if (c0 == 0 && t < nc) s_w[wv][t] = w0 * inv;
+    for (int s = (c0 == 0 ? t + 64 : t); s < nc; s += 64)
+      s_w[wv][s] = __builtin_amdgcn_exp2f(lrow[(size_t)(c0 + s) * R] - mx) * inv;
+    __builtin_amdgcn_wave_barrier();
+    int s = 0;
+    for (; s + U <= nc; s += U) {
+      f32x4 v[2 * U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const float* src = orow_acc + (size_t)(c0 + s + u) * R * kDv;
+        v[2 * u] = *(const f32x4*)src;
+        v[2 * u + 1] = *(const f32x4*)(src + 4);
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const float w = s_w[wv][s + u];
+        a0 += w * v[2 * u];
+        a1 += w * v[2 * u + 1];
+      }
+    }
+    for (; s < nc; ++s) {
+      const float* src = orow_acc + (size_t)(c0 + s) * R * kDv;
+      const float w = s_w[wv][s];
+      a0 += w * *(const f32x4*)src;
+      a1 += w * *(const f32x4*)(src + 4);
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+  bf16x2 r0 = to_bf16x2(a0[0], a0[1]);
+  bf16x2 r1 = to_bf16x2(a0[2], a0[3]);
+  bf16x2 r2 = to_bf16x2(a1[0], a1[1]);
+  bf16x2 r3 = to_bf16x2(a1[2], a1[3]);
   *(bf16x8*)orow = bf16x8{r0[0], r0[1], r1[0], r1[1], r2[0], r2[1], r3[0], r3[1]};
   if (t == 0) lse[(size_t)b * R + row] = (mx + __builtin_amdgcn_logf(z)) * kLn2;
 }
@@ -481,10 +494,7 @@ extern "C" hipError_t mla_launch_decode(const mla::DecodeParams* prm, int rows_v
       hipLaunchKernelGGL((decode_kernel<1, 1, 4>), grid, block, 0, stream, MLA_DECODE_ARGS);
       break;
     case 32:
-      hipLaunchKernelGGL((decode_kernel<1, 2, 2>), grid, block, 0, stream, MLA_DECODE_ARGS);
-      break;
-    case 64:
-      hipLaunchKernelGGL((decode_kernel<1, 4, 1>), grid, block, 0, stream, MLA_DECODE_ARGS);
+      hipLaunchKernelGGL((decode_kernel<2, 1, 4>), grid, block, 0, stream, MLA_DECODE_ARGS);
       break;
     default:
       return hipErrorInvalidValue;
@@ -496,7 +506,7 @@ extern "C" hipError_t mla_launch_decode(const mla::DecodeParams* prm, int rows_v
 extern "C" hipError_t mla_launch_combine(const float* o_acc, const float* lse_acc,
                                          const int32_t* splits, int batch, int R, uint16_t* out,
                                          float* lse, hipStream_t stream) {
-  const dim3 grid((R + 3) / 4, batch);
+  const dim3 grid((R + mla::kCombineRows - 1) / mla::kCombineRows, batch);
   hipLaunchKernelGGL(mla::combine_kernel, grid, dim3(256), 0, stream, o_acc, lse_acc, splits, R,
                      out, lse);
   return hipGetLastError();

@@ -1,0 +1,93 @@
+// Pieces shared by the decode kernels: work items, uniform values, LDS-only
+// barrier, and the HBM -> LDS page copy.
+#pragma once
+
+#include "mla_device.h"
+
+namespace mla {
+
+struct Item {
+  int b, j;
+};
+
+__device__ __forceinline__ bool item_before(Item a, int eb, int ej) {
+  return a.b < eb || (a.b == eb && a.j < ej);
+}
+
+// Wave-uniform value (kept in an SGPR, so loads indexed by it are scalar).
+__device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+// Barrier for LDS traffic only: unlike __syncthreads it does not wait for
+// outstanding global loads, so a page prefetch in flight keeps flying.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+__device__ __forceinline__ int page_slots(const int32_t* seqlens, int b) {
+  int L = uni(seqlens[b]);
+  int n = (L + kPage - 1) / kPage;
+  return n > 0 ? n : 1;
+}
+
+// Copy one 64-token page into an LDS tile.  The page is 8 blocks of 8 tokens
+// (9216 B each = 9 wave-wide 1 KiB copies); wave w copies blocks 2w and 2w+1.
+// Inside a block, copy k, lane l fills LDS chunk 64 k + l of the block:
+// token t' = (64 k + l) / 72, physical chunk p = (64 k + l) % 72, which
+// holds logical chunk p ^ swz(t').  swz depends on t & 7 only, so the nine
+// per-lane source offsets are the same for every block.
+//
+// The copy is buffer_load ... lds through a buffer resource covering exactly
+// the page (reads past it return zero).  Its global_load_lds twin makes the
+// compiler wait for every outstanding LDS operation before each LDS read
+// while a copy is in flight, which serialises the fragment pipeline below.
+struct PageLoader {
+  int off[9];  // per-lane source byte offsets inside an 8-token block
+  __device__ __forceinline__ void init(int lane) {
+#pragma unroll
+    for (int k = 0; k < 9; ++k) {
+      const int pc = 64 * k + lane;
+      const int t = pc / kChunksPerRow;
+      const int p = pc - t * kChunksPerRow;
+      off[k] = t * kRowBytes + 16 * (p ^ swz(t));
+    }
+  }
+  static __device__ __forceinline__ __amdgpu_buffer_rsrc_t resource(const char* page) {
+    return __builtin_amdgcn_make_buffer_rsrc((void*)page, (short)0, kTileBytes, kBufferFlags);
+  }
+  // Copy number i (0 .. 17) of this wave: block 2*wave + i/9, load i%9.
+  __device__ __forceinline__ void issue_one(MLA_LDS char* tile, __amdgpu_buffer_rsrc_t rsrc,
+                                            int wave, int i) const {
+    const int base = (2 * wave + i / 9) * 8 * kRowBytes;  // == 9 KiB of LDS per block
+    const int k = i % 9;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (MLA_LDS void*)(tile + base + 1024 * k), 16,
+                                             off[k], base, 0, 0);
+  }
+  // Half-page (32-token) copy: wave w copies its 8-token block w, load k.
+  __device__ __forceinline__ void issue_half(MLA_LDS char* tile, __amdgpu_buffer_rsrc_t rsrc,
+                                             int wave, int k) const {
+    const int base = wave * 8 * kRowBytes;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (MLA_LDS void*)(tile + base + 1024 * k), 16,
+                                             off[k], base, 0, 0);
+  }
+  static __device__ __forceinline__ __amdgpu_buffer_rsrc_t half_resource(const char* half) {
+    return __builtin_amdgcn_make_buffer_rsrc((void*)half, (short)0, kTileBytes / 2, kBufferFlags);
+  }
+  __device__ __forceinline__ void issue(MLA_LDS char* tile, const char* page, int wave) const {
+    const __amdgpu_buffer_rsrc_t rsrc = resource(page);
+#pragma unroll
+    for (int i = 0; i < kLoadsPerWave; ++i) issue_one(tile, rsrc, wave, i);
+  }
+};
+
+// A page copy whose 18 per-wave instructions are spread over the k-steps of
+// a score product, so the wave never stalls on a long run of memory issues.
+struct PendingCopy {
+  MLA_LDS char* tile;
+  __amdgpu_buffer_rsrc_t rsrc;
+  bool valid;
+};
+
+}  // namespace mla

@@ -26,6 +26,9 @@ constexpr int kRowGroup = 64;  // most query rows one workgroup holds
 constexpr int kMetaInts = 8;
 constexpr int kMaxParts = 4096;
 
+// Word 3 of a raw buffer resource on CDNA3/4 (32-bit data format, no swizzle).
+constexpr int kBufferFlags = 0x00020000;
+
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 // The running max used for exponentiation is only raised when a new score
@@ -53,6 +56,8 @@ __device__ __forceinline__ int swz(int t) { return t & 7; }
 // lgkmcnt [11:8].
 constexpr int kWaitVm0 = 0x0F70;    // vmcnt(0), others unconstrained
 constexpr int kWaitLgkm0 = 0xC07F;  // lgkmcnt(0), others unconstrained
+// vmcnt(9): all but the newest 9 vector-memory ops (one wave's half-page copy)
+constexpr int kWaitVm9 = 0x0F70 | 9;
 // vmcnt(18): all but the newest 18 vector-memory ops (one wave's page copy)
 constexpr int kWaitVmPrefetch = 0x0F70 | (kLoadsPerWave & 15) | ((kLoadsPerWave >> 4) << 14);
 
@@ -66,17 +71,25 @@ __device__ __forceinline__ void static_for(F&& f) {
   }
 }
 
+// Reductions over the four lanes l, l^16, l^32, l^48 that hold one query
+// row.  v_permlane16_swap / v_permlane32_swap give each lane its own value and
+// its xor-16 (xor-32) partner's, in either order; combining the two with a
+// commutative op leaves bitwise-identical results in all four lanes.  Plain
+// VALU: no trip through the LDS pipeline as a ds_bpermute shuffle would take.
 __device__ __forceinline__ float wave_max_x4(float v) {
-  // lanes l, l^16, l^32, l^48 hold the same query row
-  v = fmaxf(v, __shfl_xor(v, 16));
-  v = fmaxf(v, __shfl_xor(v, 32));
-  return v;
+  typedef __attribute__((ext_vector_type(2))) unsigned u32x2;
+  u32x2 a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  u32x2 b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
 __device__ __forceinline__ float wave_sum_x4(float v) {
-  v += __shfl_xor(v, 16);
-  v += __shfl_xor(v, 32);
-  return v;
+  typedef __attribute__((ext_vector_type(2))) unsigned u32x2;
+  u32x2 a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  u32x2 b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
 __device__ __forceinline__ bf16x2 to_bf16x2(float a, float b) {

@@ -23,17 +23,12 @@
 
 namespace mla {
 
-__device__ __forceinline__ long long floor_div(long long a, long long b) {
-  // b > 0, a >= 0 here
-  return a / b;
-}
-
+template <int NT>
 __device__ long long block_scan_exclusive(long long v, long long* total, long long* s_wave) {
-  // inclusive scan inside the wave
+  constexpr int kNW = NT / 64;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int nwaves = blockDim.x >> 6;
-  long long x = v;
+  long long x = v;  // inclusive scan inside the wave
 #pragma unroll
   for (int d = 1; d < 64; d <<= 1) {
     long long y = __shfl_up(x, d);
@@ -41,104 +36,132 @@ __device__ long long block_scan_exclusive(long long v, long long* total, long lo
   }
   if (lane == 63) s_wave[wave] = x;
   __syncthreads();
-  if (wave == 0) {
-    long long w = (lane < nwaves) ? s_wave[lane] : 0;
+  long long before = 0, tot = 0;
 #pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-      long long y = __shfl_up(w, d);
-      if (lane >= d) w += y;
-    }
-    if (lane < nwaves) s_wave[lane] = w;  // inclusive over waves
+  for (int w = 0; w < kNW; ++w) {
+    const long long sw = s_wave[w];
+    before += (w < wave) ? sw : 0;
+    tot += sw;
   }
-  __syncthreads();
-  long long before = (wave > 0) ? s_wave[wave - 1] : 0;
-  *total = s_wave[nwaves - 1];
-  __syncthreads();
+  *total = tot;
+  __syncthreads();  // s_wave is reused by the next scan
   return before + x - v;
 }
 
-__global__ void __launch_bounds__(1024) sched_kernel(const int32_t* __restrict__ seqlens,
-                                                     int batch, int num_parts, int c0,
-                                                     int32_t* __restrict__ meta,
-                                                     int32_t* __restrict__ splits) {
-  __shared__ long long s_wave[16];
+// Partition starts that fall inside sequence b's units [U, U + c), and its
+// split count.  I is int (totals below 2^31, the normal case: 32-bit
+// divisions are a short VALU sequence) or long long.
+template <typename I>
+__device__ __forceinline__ int sequence_cuts(int b, I U, I n, int c0, I q, int num_parts,
+                                             int* s_beg_b, int* s_beg_j, int* s_first) {
+  const I c = c0 + n;
+  const I A = U + c0;  // first page unit of b
+  const I a_div = A / q;
+  const I p_lo = (U + q - 1) / q;
+  I p_hi = (U + c - 1) / q;
+  if (p_hi > (I)(num_parts - 1)) p_hi = num_parts - 1;
+  for (I p = p_lo; p <= p_hi; ++p) {
+    const I u = p * q;
+    s_beg_b[p] = b;
+    s_beg_j[p] = (int)(u > A ? u - A : 0);
+    s_first[p] = (int)(u > A ? p - a_div : 0);
+  }
+  // cuts strictly inside b's page units: multiples of q in (A, A + n)
+  return (int)(1 + (A + n - 1) / q - a_div);
+}
+
+template <int NT>
+__global__ void __launch_bounds__(NT) sched_kernel(const int32_t* __restrict__ seqlens,
+                                                   int batch, int num_parts, int c0,
+                                                   int32_t* __restrict__ meta,
+                                                   int32_t* __restrict__ splits) {
+  __shared__ long long s_wave[NT / 64];
   __shared__ int s_beg_b[kMaxParts + 1];
   __shared__ int s_beg_j[kMaxParts + 1];
   __shared__ int s_first[kMaxParts + 1];
   const int tid = threadIdx.x;
-  const int nt = blockDim.x;
 
-  // pass 1: total units T
-  long long T = 0;
-  for (int base = 0; base < batch; base += nt) {
-    int b = base + tid;
-    long long c = 0;
-    if (b < batch) {
-      long long L = seqlens[b];
-      long long n = (L + kPage - 1) / kPage;
-      c = c0 + (n > 0 ? n : 1);
-    }
-    long long tot;
-    block_scan_exclusive(c, &tot, s_wave);
-    T += tot;
-  }
-  const long long q = (T + num_parts - 1) / num_parts;  // units per partition
-
-  for (int p = tid; p <= num_parts; p += nt) {
+  for (int p = tid; p <= num_parts; p += NT) {
     s_beg_b[p] = batch;
     s_beg_j[p] = 0;
     s_first[p] = 0;
   }
-  __syncthreads();
-
-  // pass 2: per-sequence split counts and the partition starts inside it
-  long long carry_u = 0, carry_s = 0;
-  for (int base = 0; base < batch; base += nt) {
-    int b = base + tid;
-    long long n = 0, c = 0;
-    if (b < batch) {
-      long long L = seqlens[b];
+  long long T = 0, q = 1;
+  if (batch <= NT) {
+    // one pass: every sequence in a register
+    long long n = 0;
+    if (tid < batch) {
+      const long long L = seqlens[tid];
       n = (L + kPage - 1) / kPage;
       if (n < 1) n = 1;
-      c = c0 + n;
     }
-    long long tot_u;
-    long long U = carry_u + block_scan_exclusive(c, &tot_u, s_wave);
-    long long ns = 0;
-    if (b < batch) {
-      const long long A = U + c0;  // first page unit of b
-      // cuts strictly inside b's page units: multiples of q in (A, A + n)
-      ns = 1 + floor_div(A + n - 1, q) - floor_div(A, q);
-      // partitions starting inside [U, U + c)
-      long long p_lo = (U + q - 1) / q;
-      long long p_hi = floor_div(U + c - 1, q);
-      for (long long p = p_lo; p <= p_hi && p < num_parts; ++p) {
-        long long u = p * q;
-        s_beg_b[p] = b;
-        s_beg_j[p] = (int)(u > A ? u - A : 0);
-        s_first[p] = (int)(u > A ? p - floor_div(A, q) : 0);
-      }
+    const long long c = tid < batch ? c0 + n : 0;
+    const long long U = block_scan_exclusive<NT>(c, &T, s_wave);  // barrier: init done
+    q = (T + num_parts - 1) / num_parts;
+    int ns = 0;
+    if (tid < batch) {
+      if (T < 0x7fffffffLL)
+        ns = sequence_cuts<int>(tid, (int)U, (int)n, c0, (int)q, num_parts, s_beg_b, s_beg_j,
+                                s_first);
+      else
+        ns = sequence_cuts<long long>(tid, U, n, c0, q, num_parts, s_beg_b, s_beg_j, s_first);
     }
     long long tot_s;
-    long long S = carry_s + block_scan_exclusive(ns, &tot_s, s_wave);
-    if (b < batch) splits[b] = (int)S;
-    carry_u += tot_u;
-    carry_s += tot_s;
+    const long long S = block_scan_exclusive<NT>(ns, &tot_s, s_wave);
+    if (tid < batch) splits[tid] = (int)S;
+    if (tid == 0) splits[batch] = (int)tot_s;
+  } else {
+    // pass 1: total units; pass 2: cuts chunk by chunk
+    for (int base = 0; base < batch; base += NT) {
+      const int b = base + tid;
+      long long c = 0;
+      if (b < batch) {
+        const long long L = seqlens[b];
+        const long long n = (L + kPage - 1) / kPage;
+        c = c0 + (n > 0 ? n : 1);
+      }
+      long long tot;
+      block_scan_exclusive<NT>(c, &tot, s_wave);
+      T += tot;
+    }
+    q = (T + num_parts - 1) / num_parts;
+    long long carry_u = 0, carry_s = 0;
+    for (int base = 0; base < batch; base += NT) {
+      const int b = base + tid;
+      long long n = 0, c = 0;
+      if (b < batch) {
+        const long long L = seqlens[b];
+        n = (L + kPage - 1) / kPage;
+        if (n < 1) n = 1;
+        c = c0 + n;
+      }
+      long long tot_u;
+      const long long U = carry_u + block_scan_exclusive<NT>(c, &tot_u, s_wave);
+      int ns = 0;
+      if (b < batch) {
+        if (T < 0x7fffffffLL)
+          ns = sequence_cuts<int>(b, (int)U, (int)n, c0, (int)q, num_parts, s_beg_b, s_beg_j,
+                                  s_first);
+        else
+          ns = sequence_cuts<long long>(b, U, n, c0, q, num_parts, s_beg_b, s_beg_j, s_first);
+      }
+      long long tot_s;
+      const long long S = carry_s + block_scan_exclusive<NT>(ns, &tot_s, s_wave);
+      if (b < batch) splits[b] = (int)S;
+      carry_u += tot_u;
+      carry_s += tot_s;
+    }
+    if (tid == 0) splits[batch] = (int)carry_s;
   }
-  if (tid == 0) splits[batch] = (int)carry_s;
   __syncthreads();
 
-  // pass 3: ranges
-  for (int p = tid; p < num_parts; p += nt) {
+  // ranges
+  for (int p = tid; p < num_parts; p += NT) {
     int32_t* m = meta + (size_t)p * kMetaInts;
-    m[0] = s_beg_b[p];
-    m[1] = s_beg_j[p];
-    m[2] = s_beg_b[p + 1];
-    m[3] = s_beg_j[p + 1];
-    m[4] = s_first[p];
-    m[5] = (int)q;
-    m[6] = c0;
-    m[7] = (int)(T < 0x7fffffffLL ? T : 0x7fffffffLL);
+    i32x4 lo = {s_beg_b[p], s_beg_j[p], s_beg_b[p + 1], s_beg_j[p + 1]};
+    i32x4 hi = {s_first[p], (int)q, c0, (int)(T < 0x7fffffffLL ? T : 0x7fffffffLL)};
+    *(i32x4*)m = lo;
+    *(i32x4*)(m + 4) = hi;
   }
 }
 
@@ -146,7 +169,11 @@ __global__ void __launch_bounds__(1024) sched_kernel(const int32_t* __restrict__
 
 extern "C" hipError_t mla_launch_sched(const int32_t* seqlens, int batch, int num_parts, int c0,
                                        int32_t* meta, int32_t* splits, hipStream_t stream) {
-  hipLaunchKernelGGL(mla::sched_kernel, dim3(1), dim3(1024), 0, stream, seqlens, batch, num_parts,
-                     c0, meta, splits);
+  if (batch <= 256)
+    hipLaunchKernelGGL(mla::sched_kernel<256>, dim3(1), dim3(256), 0, stream, seqlens, batch,
+                       num_parts, c0, meta, splits);
+  else
+    hipLaunchKernelGGL(mla::sched_kernel<1024>, dim3(1), dim3(1024), 0, stream, seqlens, batch,
+                       num_parts, c0, meta, splits);
   return hipGetLastError();
 }
