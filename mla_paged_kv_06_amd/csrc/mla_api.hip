@@ -79,7 +79,7 @@ extern "C" hipError_t mla_launch_decode(const mla::DecodeParams* prm, int rows_v
 extern "C" hipError_t mla_launch_decode_split(const mla::DecodeParams* prm, hipStream_t stream);
 extern "C" hipError_t mla_launch_combine(const float* o_acc, const float* lse_acc,
                                          const int32_t* splits, int batch, int R, uint16_t* out,
-                                         float* lse, hipStream_t stream);
+                                         float* lse, int wide, hipStream_t stream);
 
 extern "C" {
 
@@ -169,7 +169,11 @@ mla_status_t mla_combine(const void* workspace, size_t workspace_bytes, const in
   if (workspace_bytes < ws_bytes(batch, R, parts)) return MLA_ERR_WORKSPACE_TOO_SMALL;
   const float* o_acc = (const float*)workspace;
   const float* lse_acc = (const float*)((const char*)workspace + oacc_bytes(batch, R, parts));
-  hipError_t e = mla_launch_combine(o_acc, lse_acc, num_splits, batch, R, (uint16_t*)out, lse, stream);
+  // many partitions per sequence on average: spread each row's partials over
+  // a whole workgroup
+  const int wide = parts >= 8 * batch ? 1 : 0;
+  hipError_t e = mla_launch_combine(o_acc, lse_acc, num_splits, batch, R, (uint16_t*)out, lse, wide,
+                                    stream);
   return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 

@@ -1,0 +1,189 @@
+// LSE combine of split partials (FlashMLA release note, paragraph on
+// variable-length sequences: a long sequence is split over several compute
+// units, each producing a partial result whose log-sum-exp lets the partials
+// be merged exactly).
+
+#include "mla_device.h"
+
+namespace mla {
+
+// Combine: merge split partials by log-sum-exp.  One wave per query row
+// (4 rows per workgroup), 8 output columns per lane.  The weights of all
+// splits are computed first (lanes over splits, a wave max and sum), kept in
+// LDS, and the partial rows are then read with several loads in flight.
+constexpr int kCombineRows = 4;
+constexpr int kCombineChunk = 1024;  // splits whose weights sit in LDS at once
+
+__global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ o_acc,
+                                                      const float* __restrict__ lse_acc,
+                                                      const int32_t* __restrict__ splits, int R,
+                                                      uint16_t* __restrict__ out,
+                                                      float* __restrict__ lse) {
+  __shared__ float s_w[kCombineRows][kCombineChunk];
+  const int b = blockIdx.y;
+  const int wv = threadIdx.x >> 6;
+  const int row = blockIdx.x * kCombineRows + wv;
+  const int t = threadIdx.x & 63;
+  const int s0 = splits[b];
+  const int ns = splits[b + 1] - s0;
+  if (ns <= 1 || row >= R) return;  // uniform per wave; no block barrier below
+  const float* lrow = lse_acc + (size_t)s0 * R + row;
+  // the first 64 splits' lse sit in one register per lane (one load round)
+  const float l0 = t < ns ? lrow[(size_t)t * R] : -INFINITY;
+  float mx = l0;
+  for (int s = t + 64; s < ns; s += 64) mx = fmaxf(mx, lrow[(size_t)s * R]);
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) mx = fmaxf(mx, __shfl_xor(mx, d));
+  uint16_t* orow = out + ((size_t)b * R + row) * kDv + 8 * t;
+  if (mx == -INFINITY) {
+    *(i32x4*)orow = i32x4{0, 0, 0, 0};
+    if (t == 0) lse[(size_t)b * R + row] = -INFINITY;
+    return;
+  }
+  const float w0 = __builtin_amdgcn_exp2f(l0 - mx);  // -inf -> 0
+  float z = w0;
+  for (int s = t + 64; s < ns; s += 64) z += __builtin_amdgcn_exp2f(lrow[(size_t)s * R] - mx);
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) z += __shfl_xor(z, d);
+  const float inv = 1.f / z;
+  f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0;
+  const float* orow_acc = o_acc + ((size_t)s0 * R + row) * kDv + 8 * t;
+  constexpr int U = 8;  // partial rows in flight per lane
+  for (int c0 = 0; c0 < ns; c0 += kCombineChunk) {
+    const int nc = ns - c0 < kCombineChunk ? ns - c0 : kCombineChunk;
+    if (c0 == 0 && t < nc) s_w[wv][t] = w0 * inv;
+    for (int s = (c0 == 0 ? t + 64 : t); s < nc; s += 64)
+      s_w[wv][s] = __builtin_amdgcn_exp2f(lrow[(size_t)(c0 + s) * R] - mx) * inv;
+    __builtin_amdgcn_wave_barrier();
+    int s = 0;
+    for (; s + U <= nc; s += U) {
+      f32x4 v[2 * U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const float* src = orow_acc + (size_t)(c0 + s + u) * R * kDv;
+        v[2 * u] = *(const f32x4*)src;
+        v[2 * u + 1] = *(const f32x4*)(src + 4);
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const float w = s_w[wv][s + u];
+        a0 += w * v[2 * u];
+        a1 += w * v[2 * u + 1];
+      }
+    }
+    for (; s < nc; ++s) {
+      const float* src = orow_acc + (size_t)(c0 + s) * R * kDv;
+      const float w = s_w[wv][s];
+      a0 += w * *(const f32x4*)src;
+      a1 += w * *(const f32x4*)(src + 4);
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+  bf16x2 r0 = to_bf16x2(a0[0], a0[1]);
+  bf16x2 r1 = to_bf16x2(a0[2], a0[3]);
+  bf16x2 r2 = to_bf16x2(a1[0], a1[1]);
+  bf16x2 r3 = to_bf16x2(a1[2], a1[3]);
+  *(bf16x8*)orow = bf16x8{r0[0], r0[1], r1[0], r1[1], r2[0], r2[1], r3[0], r3[1]};
+  if (t == 0) lse[(size_t)b * R + row] = (mx + __builtin_amdgcn_logf(z)) * kLn2;
+}
+
+// Combine for sequences split many ways (few long sequences spread over the
+// whole GPU): one workgroup per query row, the four waves taking every fourth
+// split, so that all partial rows of a row are in flight in one round.  Each
+// wave accumulates its weighted partials (8 columns per lane); the four sums
+// meet in LDS and each wave finishes 128 columns.
+constexpr int kWideUnroll = 8;  // partial rows in flight per wave
+
+__global__ void __launch_bounds__(256) combine_wide_kernel(const float* __restrict__ o_acc,
+                                                           const float* __restrict__ lse_acc,
+                                                           const int32_t* __restrict__ splits,
+                                                           int R, uint16_t* __restrict__ out,
+                                                           float* __restrict__ lse) {
+  __shared__ f32x4 s_acc[kWaves][2][64];
+  const int b = blockIdx.y;
+  const int row = blockIdx.x;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int t = threadIdx.x & 63;
+  const int s0 = __builtin_amdgcn_readfirstlane(splits[b]);
+  const int ns = __builtin_amdgcn_readfirstlane(splits[b + 1]) - s0;
+  if (ns <= 1) return;  // uniform over the workgroup
+  const float* lrow = lse_acc + (size_t)s0 * R + row;
+  // max and sum of the split weights (lanes over splits; every wave computes
+  // the same values)
+  float mx = -INFINITY;
+  for (int s = t; s < ns; s += 64) mx = fmaxf(mx, lrow[(size_t)s * R]);
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) mx = fmaxf(mx, __shfl_xor(mx, d));
+  uint16_t* orow = out + ((size_t)b * R + row) * kDv;
+  if (mx == -INFINITY) {  // no split saw a token: uniform over the workgroup
+    if (wv == 0) {
+      *(i32x4*)(orow + 8 * t) = i32x4{0, 0, 0, 0};
+      if (t == 0) lse[(size_t)b * R + row] = -INFINITY;
+    }
+    return;
+  }
+  float z = 0.f;
+  for (int s = t; s < ns; s += 64) z += __builtin_amdgcn_exp2f(lrow[(size_t)s * R] - mx);
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) z += __shfl_xor(z, d);
+  const float inv = 1.f / z;
+  // this wave's splits: wv, wv + 4, ...
+  f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0;
+  const float* base = o_acc + ((size_t)s0 * R + row) * kDv + 8 * t;
+  for (int s = wv; s < ns; s += kWaves * kWideUnroll) {
+    f32x4 v[2 * kWideUnroll];
+    float w[kWideUnroll];
+#pragma unroll
+    for (int u = 0; u < kWideUnroll; ++u) {
+      const int si = s + kWaves * u;
+      if (si < ns) {
+        const float* src = base + (size_t)si * R * kDv;
+        v[2 * u] = *(const f32x4*)src;
+        v[2 * u + 1] = *(const f32x4*)(src + 4);
+        w[u] = __builtin_amdgcn_exp2f(lrow[(size_t)si * R] - mx) * inv;
+      } else {
+        v[2 * u] = v[2 * u + 1] = f32x4{0.f, 0.f, 0.f, 0.f};
+        w[u] = 0.f;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kWideUnroll; ++u) {
+      a0 += w[u] * v[2 * u];
+      a1 += w[u] * v[2 * u + 1];
+    }
+  }
+  s_acc[wv][0][t] = a0;
+  s_acc[wv][1][t] = a1;
+  __syncthreads();
+  // wave wv finishes columns 128 wv .. 128 wv + 127: lane t < 32 takes the
+  // four columns held by source lane 16 wv + t / 2, half t & 1
+  if (t < 32) {
+    const int src = 16 * wv + (t >> 1);
+    const int h = t & 1;
+    f32x4 acc = s_acc[0][h][src];
+#pragma unroll
+    for (int k = 1; k < kWaves; ++k) acc += s_acc[k][h][src];
+    const bf16x2 x = to_bf16x2(acc[0], acc[1]);
+    const bf16x2 y = to_bf16x2(acc[2], acc[3]);
+    *(bf16x4*)(orow + 8 * src + 4 * h) = bf16x4{x[0], x[1], y[0], y[1]};
+  }
+  if (wv == 0 && t == 0) lse[(size_t)b * R + row] = (mx + __builtin_amdgcn_logf(z)) * kLn2;
+}
+
+}  // namespace mla
+
+// wide: the caller's estimate that sequences are split many ways (partitions
+// well above the batch); the result is the same either way.
+extern "C" hipError_t mla_launch_combine(const float* o_acc, const float* lse_acc,
+                                         const int32_t* splits, int batch, int R, uint16_t* out,
+                                         float* lse, int wide, hipStream_t stream) {
+  if (wide) {
+    hipLaunchKernelGGL(mla::combine_wide_kernel, dim3(R, batch), dim3(256), 0, stream, o_acc,
+                       lse_acc, splits, R, out, lse);
+  } else {
+    const dim3 grid((R + mla::kCombineRows - 1) / mla::kCombineRows, batch);
+    hipLaunchKernelGGL(mla::combine_kernel, grid, dim3(256), 0, stream, o_acc, lse_acc, splits, R,
+                       out, lse);
+  }
+  return hipGetLastError();
+}

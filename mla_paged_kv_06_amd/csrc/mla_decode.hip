@@ -121,6 +121,9 @@ __global__ void __launch_bounds__(kThreads, 1)
   float m_used[RT], l_part[RT];
   int n_vis[RT];
   int L = 0;
+  // split bookkeeping of the current sequence, fetched when it begins so that
+  // the epilogue does not wait for a load
+  int seg_s_lo = 0, seg_nsplit = 0;
 
   const char* kvbase = (const char*)kv_ptr;
   PageLoader loader;
@@ -128,6 +131,8 @@ __global__ void __launch_bounds__(kThreads, 1)
 
   auto begin_segment = [&](int b) __attribute__((always_inline)) {
     L = uni(seqlens[b]);
+    seg_s_lo = uni(splits[b]);
+    seg_nsplit = uni(splits[b + 1]) - seg_s_lo;
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
       const int row = row_base + 16 * rt + l16;
@@ -322,8 +327,8 @@ __global__ void __launch_bounds__(kThreads, 1)
   };
 
   auto finish_segment = [&](int b) __attribute__((always_inline)) {
-    const int s_lo = uni(splits[b]);
-    const int nsplit = uni(splits[b + 1]) - s_lo;
+    const int s_lo = seg_s_lo;
+    const int nsplit = seg_nsplit;
     const bool direct = nsplit <= 1;
     const int slot = s_lo + split_idx;
 #pragma unroll
@@ -395,87 +400,6 @@ __global__ void __launch_bounds__(kThreads, 1)
   }
 }
 
-// ---------------------------------------------------------------------------
-// Combine: merge split partials by log-sum-exp.  One wave per query row
-// (4 rows per workgroup), 8 output columns per lane.  The weights of all
-// splits are computed first (lanes over splits, a wave max and sum), kept in
-// LDS, and the partial rows are then read with several loads in flight.
-constexpr int kCombineRows = 4;
-constexpr int kCombineChunk = 1024;  // splits whose weights sit in LDS at once
-
-__global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ o_acc,
-                                                      const float* __restrict__ lse_acc,
-                                                      const int32_t* __restrict__ splits, int R,
-                                                      uint16_t* __restrict__ out,
-                                                      float* __restrict__ lse) {
-  __shared__ float s_w[kCombineRows][kCombineChunk];
-  const int b = blockIdx.y;
-  const int wv = threadIdx.x >> 6;
-  const int row = blockIdx.x * kCombineRows + wv;
-  const int t = threadIdx.x & 63;
-  const int s0 = splits[b];
-  const int ns = splits[b + 1] - s0;
-  if (ns <= 1 || row >= R) return;  // uniform per wave; no block barrier below
-  const float* lrow = lse_acc + (size_t)s0 * R + row;
-  // the first 64 splits' lse sit in one register per lane (one load round)
-  const float l0 = t < ns ? lrow[(size_t)t * R] : -INFINITY;
-  float mx = l0;
-  for (int s = t + 64; s < ns; s += 64) mx = fmaxf(mx, lrow[(size_t)s * R]);
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) mx = fmaxf(mx, __shfl_xor(mx, d));
-  uint16_t* orow = out + ((size_t)b * R + row) * kDv + 8 * t;
-  if (mx == -INFINITY) {
-    *(i32x4*)orow = i32x4{0, 0, 0, 0};
-    if (t == 0) lse[(size_t)b * R + row] = -INFINITY;
-    return;
-  }
-  const float w0 = __builtin_amdgcn_exp2f(l0 - mx);  // -inf -> 0
-  float z = w0;
-  for (int s = t + 64; s < ns; s += 64) z += __builtin_amdgcn_exp2f(lrow[(size_t)s * R] - mx);
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) z += __shfl_xor(z, d);
-  const float inv = 1.f / z;
-  f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0;
-  const float* orow_acc = o_acc + ((size_t)s0 * R + row) * kDv + 8 * t;
-  constexpr int U = 8;  // partial rows in flight per lane
-  for (int c0 = 0; c0 < ns; c0 += kCombineChunk) {
-    const int nc = ns - c0 < kCombineChunk ? ns - c0 : kCombineChunk;
-    if (c0 == 0 && t < nc) s_w[wv][t] = w0 * inv;
-    for (int s = (c0 == 0 ? t + 64 : t); s < nc; s += 64)
-      s_w[wv][s] = __builtin_amdgcn_exp2f(lrow[(size_t)(c0 + s) * R] - mx) * inv;
-    __builtin_amdgcn_wave_barrier();
-    int s = 0;
-    for (; s + U <= nc; s += U) {
-      f32x4 v[2 * U];
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const float* src = orow_acc + (size_t)(c0 + s + u) * R * kDv;
-        v[2 * u] = *(const f32x4*)src;
-        v[2 * u + 1] = *(const f32x4*)(src + 4);
-      }
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const float w = s_w[wv][s + u];
-        a0 += w * v[2 * u];
-        a1 += w * v[2 * u + 1];
-      }
-    }
-    for (; s < nc; ++s) {
-      const float* src = orow_acc + (size_t)(c0 + s) * R * kDv;
-      const float w = s_w[wv][s];
-      a0 += w * *(const f32x4*)src;
-      a1 += w * *(const f32x4*)(src + 4);
-    }
-    __builtin_amdgcn_wave_barrier();
-  }
-  bf16x2 r0 = to_bf16x2(a0[0], a0[1]);
-  bf16x2 r1 = to_bf16x2(a0[2], a0[3]);
-  bf16x2 r2 = to_bf16x2(a1[0], a1[1]);
-  bf16x2 r3 = to_bf16x2(a1[2], a1[3]);
-  *(bf16x8*)orow = bf16x8{r0[0], r0[1], r1[0], r1[1], r2[0], r2[1], r3[0], r3[1]};
-  if (t == 0) lse[(size_t)b * R + row] = (mx + __builtin_amdgcn_logf(z)) * kLn2;
-}
-
 }  // namespace mla
 
 // ---------------------------------------------------------------------------
@@ -500,14 +424,5 @@ extern "C" hipError_t mla_launch_decode(const mla::DecodeParams* prm, int rows_v
       return hipErrorInvalidValue;
   }
 #undef MLA_DECODE_ARGS
-  return hipGetLastError();
-}
-
-extern "C" hipError_t mla_launch_combine(const float* o_acc, const float* lse_acc,
-                                         const int32_t* splits, int batch, int R, uint16_t* out,
-                                         float* lse, hipStream_t stream) {
-  const dim3 grid((R + mla::kCombineRows - 1) / mla::kCombineRows, batch);
-  hipLaunchKernelGGL(mla::combine_kernel, grid, dim3(256), 0, stream, o_acc, lse_acc, splits, R,
-                     out, lse);
   return hipGetLastError();
 }

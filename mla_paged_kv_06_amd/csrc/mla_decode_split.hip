@@ -81,6 +81,9 @@ __global__ void __launch_bounds__(kThreads, 1)
   float m_used = -INFINITY, l_part = 0.f;
   int n_vis = 0;
   int L = 0;
+  // split bookkeeping of the current sequence, fetched when it begins so that
+  // the epilogue does not wait for a load
+  int seg_s_lo = 0, seg_nsplit = 0;
 
   const char* kvbase = (const char*)kv_ptr;
   PageLoader loader;
@@ -88,6 +91,8 @@ __global__ void __launch_bounds__(kThreads, 1)
 
   auto begin_segment = [&](int b) __attribute__((always_inline)) {
     L = uni(seqlens[b]);
+    seg_s_lo = uni(splits[b]);
+    seg_nsplit = uni(splits[b + 1]) - seg_s_lo;
     const bool live = qk_row < prm.R;
     // rows past R read row 0 and are never stored; they see no tokens
     const uint16_t* qrow = q_ptr + ((size_t)b * prm.R + (live ? qk_row : 0)) * kD + 8 * g;
@@ -258,8 +263,8 @@ __global__ void __launch_bounds__(kThreads, 1)
   };
 
   auto finish_segment = [&](int b) __attribute__((always_inline)) {
-    const int s_lo = uni(splits[b]);
-    const int nsplit = uni(splits[b + 1]) - s_lo;
+    const int s_lo = seg_s_lo;
+    const int nsplit = seg_nsplit;
     const bool direct = nsplit <= 1;
     const int slot = s_lo + split_idx;
     // the scoring wave of each row publishes its sum, and writes its lse
