@@ -127,6 +127,8 @@ mla_status_t mla_get_metadata(const int32_t* cache_seqlens, int32_t batch, int32
  * written straight to out/lse; the others write float32 partials into the
  * workspace for mla_combine.  tile_metadata and num_splits must come from
  * mla_get_metadata with the same cache_seqlens, batch, s_q, h_q and num_cus.
+ * softmax_scale must be finite and positive (the pages' 1/sqrt(d) scaling);
+ * anything else returns MLA_ERR_INVALID_ARGUMENT.
  */
 mla_status_t mla_decode_paged(const void* q, const void* kv_cache, const int32_t* block_table,
                               const int32_t* cache_seqlens, int32_t batch, int32_t s_q,

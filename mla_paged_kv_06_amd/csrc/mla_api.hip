@@ -122,7 +122,7 @@ mla_status_t mla_decode_paged(const void* q, const void* kv_cache, const int32_t
     return MLA_ERR_INVALID_ARGUMENT;
   if (batch <= 0 || s_q <= 0 || h_q <= 0 || num_pages <= 0 || max_pages <= 0 || num_cus < 0)
     return MLA_ERR_INVALID_ARGUMENT;
-  if (!std::isfinite(softmax_scale)) return MLA_ERR_INVALID_ARGUMENT;
+  if (!std::isfinite(softmax_scale) || !(softmax_scale > 0.f)) return MLA_ERR_INVALID_ARGUMENT;
   if (batch > MLA_MAX_BATCH || !rows_ok(s_q, h_q)) return MLA_ERR_UNSUPPORTED;
   if (((uintptr_t)q | (uintptr_t)kv_cache | (uintptr_t)out | (uintptr_t)workspace) & 15)
     return MLA_ERR_INVALID_ARGUMENT;

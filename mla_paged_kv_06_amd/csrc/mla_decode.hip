@@ -159,7 +159,7 @@ __global__ void __launch_bounds__(kThreads, 1)
     const int L_it = uni(seqlens[it.b]);
     if (it.j * kPage >= L_it) return false;
     const int phys = uni(block_table[(size_t)it.b * prm.max_pages + it.j]);
-    loader.issue(tile, kvbase + (size_t)phys * kTileBytes, wave);
+    loader.issue(tile, kvbase + (size_t)phys * kTileBytes, L_it - it.j * kPage, wave);
     return true;
   };
 
@@ -168,21 +168,23 @@ __global__ void __launch_bounds__(kThreads, 1)
     PendingCopy cp;
     cp.tile = tile;
     cp.valid = false;
-    cp.rsrc = PageLoader::resource(kvbase);
+    cp.rsrc = PageLoader::resource(kvbase, 0);
     if (has) {
       const int L_it = uni(seqlens[it.b]);
       if (it.j * kPage < L_it) {
         const int phys = uni(block_table[(size_t)it.b * prm.max_pages + it.j]);
-        cp.rsrc = PageLoader::resource(kvbase + (size_t)phys * kTileBytes);
+        cp.rsrc = PageLoader::resource(kvbase + (size_t)phys * kTileBytes, L_it - it.j * kPage);
         cp.valid = true;
       }
     }
     return cp;
   };
 
+  // next item after `it` of the current sequence (whose length is L)
   auto advance = [&](Item it) __attribute__((always_inline)) {
     Item nx = it;
-    if (it.j + 1 < page_slots(seqlens, it.b)) {
+    const int n_slots = (L + kPage - 1) / kPage;
+    if (it.j + 1 < (n_slots > 0 ? n_slots : 1)) {
       nx.j = uni(it.j + 1);
     } else {
       nx.b = uni(it.b + 1);
@@ -231,9 +233,13 @@ __global__ void __launch_bounds__(kThreads, 1)
     static_for<0, KS>([&](auto ksc) __attribute__((always_inline)) {
       constexpr int ks = decltype(ksc)::value;
       if constexpr (ks + DK < KS) load_k(kr[(ks + DK) % (DK + 1)], ks + DK);
-      if constexpr (h == 0) {
-        static_assert(KS == kLoadsPerWave, "one page-copy instruction per k-step");
-        if (cp.valid) loader.issue_one(cp.tile, cp.rsrc, wave, ks);
+      // the next page's 18 copy instructions go out at every other k-step of
+      // both halves: issued in one burst they outrun the CU's address unit
+      // (16 cycles per 1 KiB instruction, four waves sharing it) and stall
+      // the wave, and the matrix pipe with it
+      if constexpr (ks % 2 == 0) {
+        static_assert(KS == kLoadsPerWave, "nine copies per half, at the even k-steps");
+        if (cp.valid) loader.issue_one(cp.tile, cp.rsrc, wave, 9 * h + ks / 2);
       }
       mma_k(kr[ks % (DK + 1)], ks);
       __builtin_amdgcn_sched_barrier(0);
@@ -318,14 +324,6 @@ __global__ void __launch_bounds__(kThreads, 1)
     compute_half(tile, j, std::integral_constant<int, 1>{}, cp);
   };
 
-  auto zero_tail = [&](MLA_LDS char* tile, int first_dead) __attribute__((always_inline)) {
-    // tokens first_dead..63 of the tile may hold anything (a real allocator
-    // does not clear pages); zero them so 0-weight x garbage cannot give NaN
-    const int start = first_dead * kRowBytes;
-    for (int off = start + threadIdx.x * 16; off < kTileBytes; off += kThreads * 16)
-      *(MLA_LDS i32x4*)(tile + off) = i32x4{0, 0, 0, 0};
-  };
-
   auto finish_segment = [&](int b) __attribute__((always_inline)) {
     const int s_lo = seg_s_lo;
     const int nsplit = seg_nsplit;
@@ -370,16 +368,13 @@ __global__ void __launch_bounds__(kThreads, 1)
   auto step = [&](MLA_LDS char* tA, MLA_LDS char* tB) __attribute__((always_inline)) -> bool {
     const Item nx = advance(cur);
     const bool has_next = item_before(nx, eb, ej);
+    // descriptor of the next copy first: its scalar loads (block table and
+    // lengths, never written here) overlap the wait below
+    PendingCopy cp = next_copy(tB, nx, has_next);
     __builtin_amdgcn_s_waitcnt(kWaitVm0);  // this wave's part of tile A landed
     __syncthreads();                       // ... and every wave's; B is free
-    PendingCopy cp = next_copy(tB, nx, has_next);
     const bool has_tokens = cur.j * kPage < L;
     if (has_tokens) {
-      const int live = L - cur.j * kPage;
-      if (live < kPage) {
-        zero_tail(tA, live);
-        lds_barrier();
-      }
       compute_page(tA, cur.j, cp);
     } else if (cp.valid) {
       for (int i = 0; i < kLoadsPerWave; ++i) loader.issue_one(cp.tile, cp.rsrc, wave, i);

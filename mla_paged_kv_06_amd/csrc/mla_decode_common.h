@@ -26,14 +26,10 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
 }
 
-__device__ __forceinline__ int page_slots(const int32_t* seqlens, int b) {
-  int L = uni(seqlens[b]);
-  int n = (L + kPage - 1) / kPage;
-  return n > 0 ? n : 1;
-}
-
 // Copy one 64-token page into an LDS tile.  The page is 8 blocks of 8 tokens
-// (9216 B each = 9 wave-wide 1 KiB copies); wave w copies blocks 2w and 2w+1.
+// (9216 B each = 9 wave-wide 1 KiB copies); wave w copies block w (first
+// half page) with its copies 0..8 and block w + 4 (second half) with 9..17,
+// so a wave's first nine copies complete the first half of the page.
 // Inside a block, copy k, lane l fills LDS chunk 64 k + l of the block:
 // token t' = (64 k + l) / 72, physical chunk p = (64 k + l) % 72, which
 // holds logical chunk p ^ swz(t').  swz depends on t & 7 only, so the nine
@@ -54,32 +50,89 @@ struct PageLoader {
       off[k] = t * kRowBytes + 16 * (p ^ swz(t));
     }
   }
-  static __device__ __forceinline__ __amdgpu_buffer_rsrc_t resource(const char* page) {
-    return __builtin_amdgcn_make_buffer_rsrc((void*)page, (short)0, kTileBytes, kBufferFlags);
+  // Resource for a page of which `live` tokens (1..64) hold data: reads past
+  // them return zero, so the tail of a sequence's last page arrives in LDS
+  // already cleared (a zero weight times stale data could otherwise be NaN).
+  static __device__ __forceinline__ __amdgpu_buffer_rsrc_t resource(const char* page, int live) {
+    const int n = live < kPage ? live : kPage;
+    return __builtin_amdgcn_make_buffer_rsrc((void*)page, (short)0, n * kRowBytes, kBufferFlags);
   }
-  // Copy number i (0 .. 17) of this wave: block 2*wave + i/9, load i%9.
+  // Copy number i (0 .. 17) of this wave: block wave + 4 (i / 9), load i % 9.
   __device__ __forceinline__ void issue_one(MLA_LDS char* tile, __amdgpu_buffer_rsrc_t rsrc,
                                             int wave, int i) const {
-    const int base = (2 * wave + i / 9) * 8 * kRowBytes;  // == 9 KiB of LDS per block
+    const int base = (wave + 4 * (i / 9)) * 8 * kRowBytes;  // == 9 KiB of LDS per block
     const int k = i % 9;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (MLA_LDS void*)(tile + base + 1024 * k), 16,
                                              off[k], base, 0, 0);
   }
-  // Half-page (32-token) copy: wave w copies its 8-token block w, load k.
-  __device__ __forceinline__ void issue_half(MLA_LDS char* tile, __amdgpu_buffer_rsrc_t rsrc,
-                                             int wave, int k) const {
-    const int base = wave * 8 * kRowBytes;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (MLA_LDS void*)(tile + base + 1024 * k), 16,
-                                             off[k], base, 0, 0);
-  }
-  static __device__ __forceinline__ __amdgpu_buffer_rsrc_t half_resource(const char* half) {
-    return __builtin_amdgcn_make_buffer_rsrc((void*)half, (short)0, kTileBytes / 2, kBufferFlags);
-  }
-  __device__ __forceinline__ void issue(MLA_LDS char* tile, const char* page, int wave) const {
-    const __amdgpu_buffer_rsrc_t rsrc = resource(page);
+  __device__ __forceinline__ void issue(MLA_LDS char* tile, const char* page, int live,
+                                        int wave) const {
+    const __amdgpu_buffer_rsrc_t rsrc = resource(page, live);
 #pragma unroll
     for (int i = 0; i < kLoadsPerWave; ++i) issue_one(tile, rsrc, wave, i);
   }
+};
+
+// Raw buffer resource (CDNA3/4 layout) as four SGPRs: 48-bit base, stride 0,
+// size in bytes, 32-bit format flags.  Reads at offsets >= size return zero.
+__device__ __forceinline__ i32x4 buffer_desc(const char* base, int bytes) {
+  const unsigned long long a = (unsigned long long)base;
+  return i32x4{uni((int)(unsigned)a), uni((int)((a >> 32) & 0xFFFF)), uni(bytes), kBufferFlags};
+}
+
+// One wave-wide copy HBM -> LDS, 16 bytes per lane: lane l's bytes at offset
+// voff + soff of the resource go to LDS address lds_base + 16 l.  Written in
+// assembly so that the compiler does not track it: it returns nothing to
+// registers, and the kernels that use it wait for it with explicit, fenced
+// s_waitcnt only (the compiler cannot tell which half of a tile a copy
+// writes and would otherwise wait for whole tiles).  M0 carries the LDS base;
+// no compiled code in these kernels uses M0.  The five wait states cover SGPR
+// operands written by VALU (readfirstlane) just before.
+__device__ __forceinline__ void copy16_to_lds(MLA_LDS char* lds_base, int voff, i32x4 desc,
+                                              int soff) {
+  const int m0 = uni((int)(size_t)lds_base);
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 4\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               :
+               : "s"(m0), "v"(voff), "s"(desc), "s"(soff)
+               : "memory", "m0");
+}
+
+// s_waitcnt between compiler fences: the wait intrinsic alone does not keep
+// the scheduler from moving LDS reads above it.
+template <int kImm>
+__device__ __forceinline__ void fenced_wait() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(kImm);
+  asm volatile("" ::: "memory");
+}
+
+// The page copy of PageLoader through copy16_to_lds.
+struct AsmPageLoader {
+  int off[9];
+  __device__ __forceinline__ void init(int lane) {
+#pragma unroll
+    for (int k = 0; k < 9; ++k) {
+      const int pc = 64 * k + lane;
+      const int t = pc / kChunksPerRow;
+      const int p = pc - t * kChunksPerRow;
+      off[k] = t * kRowBytes + 16 * (p ^ swz(t));
+    }
+  }
+  static __device__ __forceinline__ i32x4 desc(const char* page, int live) {
+    const int n = live < kPage ? live : kPage;
+    return buffer_desc(page, n * kRowBytes);
+  }
+  // copy i (0 .. 17): block wave + 4 (i / 9), load i % 9
+  __device__ __forceinline__ void issue_one(MLA_LDS char* tile, i32x4 d, int wave, int i) const {
+    const int base = (wave + 4 * (i / 9)) * 8 * kRowBytes;
+    copy16_to_lds(tile + base + 1024 * (i % 9), off[i % 9], d, base);
+  }
+};
+
+struct AsmPendingCopy {
+  MLA_LDS char* tile;
+  i32x4 desc;
+  bool valid;
 };
 
 // A page copy whose 18 per-wave instructions are spread over the k-steps of

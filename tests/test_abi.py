@@ -91,6 +91,9 @@ def test_invalid_arguments_launch_nothing(lib):
     assert lib.mla_decode_paged(*bad) == 1
     bad = list(args); bad[9] = float("nan")
     assert lib.mla_decode_paged(*bad) == 1
+    for scale in (0.0, -0.1, float("-inf")):  # the scale must be finite and positive
+        bad = list(args); bad[9] = scale
+        assert lib.mla_decode_paged(*bad) == 1
     bad = list(args); bad[7] = 0  # num_pages
     assert lib.mla_decode_paged(*bad) == 1
     bad = list(args); bad[15] = 100  # workspace too small

@@ -194,6 +194,8 @@ def test_error_codes(mla):
     meta, splits = mla.get_metadata(sl, 1, 16)
     with pytest.raises(mla.MlaError):
         mla.decode_paged(q, kv, bt, sl, float("inf"), False, meta, splits)
+    with pytest.raises(mla.MlaError):
+        mla.decode_paged(q, kv, bt, sl, 0.0, False, meta, splits)
     small = torch.empty((64,), dtype=torch.uint8, device="cuda:0")
     with pytest.raises(mla.MlaError) as e:
         mla.decode_paged(q, kv, bt, sl, 0.1, False, meta, splits, workspace=small)
