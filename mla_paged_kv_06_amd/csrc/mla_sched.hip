@@ -165,13 +165,138 @@ __global__ void __launch_bounds__(NT) sched_kernel(const int32_t* __restrict__ s
   }
 }
 
+// Inclusive prefix sum over the block, one value per thread; the block total
+// lands in *total.  Two barriers.
+template <int NT, typename I>
+__device__ __forceinline__ I block_scan_inclusive(I v, I* total, I* s_wave) {
+  constexpr int kNW = NT / 64;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  I x = v;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const I y = __shfl_up(x, d);
+    if (lane >= d) x += y;
+  }
+  if (lane == 63) s_wave[wave] = x;
+  __syncthreads();
+  I before = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < kNW; ++w) {
+    const I sw = s_wave[w];
+    before += (w < wave) ? sw : 0;
+    tot += sw;
+  }
+  *total = tot;
+  __syncthreads();  // s_wave is reused by the next scan
+  return before + x;
+}
+
+// Body of sched_small_kernel in index type I (int when every total is below
+// 2^31, long long otherwise): the same rule as sched_kernel, with no serial
+// loop -- each partition p finds the sequence holding its start unit p*q by
+// binary search over the unit prefix sums.
+template <int NT, typename I>
+__device__ __forceinline__ void sched_small_body(int n, int batch, int num_parts, int c0,
+                                                 int32_t* __restrict__ meta,
+                                                 int32_t* __restrict__ splits, I* s_U,
+                                                 I* s_wave, i32x2* s_start) {
+  const int tid = threadIdx.x;
+  const I c = tid < batch ? (I)(c0 + n) : (I)0;
+  I T;
+  const I U = block_scan_inclusive<NT, I>(c, &T, s_wave) - c;
+  if (tid < batch) s_U[tid] = U;
+  const I q = (T + num_parts - 1) / num_parts;
+  // splits of sequence b: its start partition plus the cuts strictly inside
+  // its page units (multiples of q in (A, A + n))
+  I ns = 0;
+  if (tid < batch) {
+    const I A = U + c0;
+    ns = 1 + (A + n - 1) / q - A / q;
+  }
+  I S_tot;
+  const I S = block_scan_inclusive<NT, I>(ns, &S_tot, s_wave) - ns;  // barriers: s_U complete
+  if (tid < batch) splits[tid] = (int32_t)S;
+  if (tid == 0) splits[batch] = (int32_t)S_tot;
+  // start (sequence, page, split index) of partition p
+  auto start_of = [&](int p, int* b_out, int* j_out, int* f_out) {
+    const I u = (I)p * q;
+    if (u >= T) {
+      *b_out = batch;
+      *j_out = 0;
+      *f_out = 0;
+      return;
+    }
+    int lo = 0, hi = batch - 1;  // largest b with U[b] <= u
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (s_U[mid] <= u) lo = mid; else hi = mid - 1;
+    }
+    const I A = s_U[lo] + c0;
+    *b_out = lo;
+    *j_out = (int)(u > A ? u - A : 0);
+    *f_out = (int)(u > A ? p - A / q : 0);
+  };
+  const int T32 = (int)(T < (I)0x7fffffff ? T : (I)0x7fffffff);
+  // one search per partition: thread t finds the start of partition
+  // base + t; the end of partition p is the start of p + 1, taken from the
+  // neighbouring thread through LDS (the last thread searches it itself)
+  for (int base = 0; base < num_parts; base += NT) {
+    const int p = base + tid;
+    int b0 = batch, j0 = 0, f0 = 0;
+    if (p <= num_parts) start_of(p, &b0, &j0, &f0);
+    s_start[tid] = i32x2{b0, j0};
+    int b1 = batch, j1 = 0, f1 = 0;
+    if (tid == NT - 1 && p + 1 <= num_parts) start_of(p + 1, &b1, &j1, &f1);
+    __syncthreads();
+    if (tid < NT - 1) {
+      b1 = s_start[tid + 1][0];
+      j1 = s_start[tid + 1][1];
+    }
+    if (p < num_parts) {
+      int32_t* m = meta + (size_t)p * kMetaInts;
+      *(i32x4*)m = i32x4{b0, j0, b1, j1};
+      *(i32x4*)(m + 4) = i32x4{f0, (int)q, c0, T32};
+    }
+    __syncthreads();  // s_start is reused by the next round
+  }
+}
+
+template <int NT>
+__global__ void __launch_bounds__(NT) sched_small_kernel(const int32_t* __restrict__ seqlens,
+                                                         int batch, int num_parts, int c0,
+                                                         int32_t* __restrict__ meta,
+                                                         int32_t* __restrict__ splits) {
+  __shared__ long long s_U[NT];
+  __shared__ long long s_wave[NT / 64];
+  __shared__ i32x2 s_start[NT];
+  const int tid = threadIdx.x;
+  int n = 0;
+  if (tid < batch) {
+    const int L = seqlens[tid];
+    n = (L + kPage - 1) / kPage;
+    if (n < 1) n = 1;
+  }
+  // fewer than 2^20 units per sequence and at most 1024 sequences keep every
+  // total below 2^30: 32-bit arithmetic is exact
+  if (!__syncthreads_or(n >= (1 << 20) - 8))
+    sched_small_body<NT, int>(n, batch, num_parts, c0, meta, splits, (int*)s_U, (int*)s_wave,
+                              s_start);
+  else
+    sched_small_body<NT, long long>(n, batch, num_parts, c0, meta, splits, s_U, s_wave, s_start);
+}
+
 }  // namespace mla
 
 extern "C" hipError_t mla_launch_sched(const int32_t* seqlens, int batch, int num_parts, int c0,
                                        int32_t* meta, int32_t* splits, hipStream_t stream) {
+  // at least 256 threads: one partition per thread in the common case
   if (batch <= 256)
-    hipLaunchKernelGGL(mla::sched_kernel<256>, dim3(1), dim3(256), 0, stream, seqlens, batch,
-                       num_parts, c0, meta, splits);
+    hipLaunchKernelGGL(mla::sched_small_kernel<256>, dim3(1), dim3(256), 0, stream, seqlens,
+                       batch, num_parts, c0, meta, splits);
+  else if (batch <= 1024)
+    hipLaunchKernelGGL(mla::sched_small_kernel<1024>, dim3(1), dim3(1024), 0, stream, seqlens,
+                       batch, num_parts, c0, meta, splits);
   else
     hipLaunchKernelGGL(mla::sched_kernel<1024>, dim3(1), dim3(1024), 0, stream, seqlens, batch,
                        num_parts, c0, meta, splits);

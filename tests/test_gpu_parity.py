@@ -174,6 +174,38 @@ def test_device_schedule_matches_model(mla, s_q, h_q, num_cus):
     _say(f"[sched] s_q={s_q} h_q={h_q} num_cus={num_cus}")
     rng = np.random.Generator(np.random.PCG64(43))
     L = list(rng.integers(0, 20000, size=37)) + [131072, 0, 1, 64]
+    _check_schedule(mla, L, s_q, h_q, num_cus)
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("batch", [1, 64, 65, 200, 256, 257, 700, 1024, 1025, 1500])
+def test_device_schedule_batch_sizes(mla, batch):
+    """Every scheduler path (one workgroup of 64, 256 or 1024 threads, and the
+    chunked path past 1024 sequences) against the model."""
+    _say(f"[sched] batch={batch}")
+    rng = np.random.Generator(np.random.PCG64(1000 + batch))
+    L = [int(x) for x in rng.integers(0, 9000, size=batch)]
+    L[0] = 0
+    for num_cus in (0, 7, 1024):
+        _check_schedule(mla, L, 1, 16, num_cus)
+        _check_schedule(mla, L, 2, 128, num_cus)
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("batch", [3, 100, 600])
+def test_device_schedule_huge_lengths(mla, batch):
+    """A sequence of 2^26+ tokens (2^20 page units) takes the 64-bit
+    arithmetic of the small-batch scheduler; only the schedule is computed."""
+    _say(f"[sched] huge lengths, batch={batch}")
+    rng = np.random.Generator(np.random.PCG64(7 + batch))
+    L = [int(x) for x in rng.integers(0, 5000, size=batch)]
+    L[batch // 2] = 70_000_000
+    L[-1] = 2**26 + 5
+    for num_cus in (0, 13):
+        _check_schedule(mla, L, 1, 64, num_cus)
+
+
+def _check_schedule(mla, L, s_q, h_q, num_cus):
     sl = torch.tensor(L, dtype=torch.int32, device="cuda:0")
     meta, splits = mla.get_metadata(sl, s_q, h_q, num_cus)
     torch.cuda.synchronize()
