@@ -17,7 +17,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libmla_paged.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 
-SOURCES = ["mla_api.hip", "mla_sched.hip", "mla_decode.hip", "mla_decode_split.hip",
+SOURCES = ["mla_api.hip", "mla_sched.hip", "mla_decode.hip", "mla_decode_split8.hip",
            "mla_combine.hip"]
 
 HIP_FLAGS = [
@@ -29,8 +29,6 @@ HIP_FLAGS = [
     # packed fp32 VALU ops are kept out of every kernel
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wno-unused-command-line-argument",
-    # the page copies write M0 in inline assembly; no compiled code uses M0
-    "-Wno-inline-asm",
 ]
 
 

@@ -73,68 +73,6 @@ struct PageLoader {
   }
 };
 
-// Raw buffer resource (CDNA3/4 layout) as four SGPRs: 48-bit base, stride 0,
-// size in bytes, 32-bit format flags.  Reads at offsets >= size return zero.
-__device__ __forceinline__ i32x4 buffer_desc(const char* base, int bytes) {
-  const unsigned long long a = (unsigned long long)base;
-  return i32x4{uni((int)(unsigned)a), uni((int)((a >> 32) & 0xFFFF)), uni(bytes), kBufferFlags};
-}
-
-// One wave-wide copy HBM -> LDS, 16 bytes per lane: lane l's bytes at offset
-// voff + soff of the resource go to LDS address lds_base + 16 l.  Written in
-// assembly so that the compiler does not track it: it returns nothing to
-// registers, and the kernels that use it wait for it with explicit, fenced
-// s_waitcnt only (the compiler cannot tell which half of a tile a copy
-// writes and would otherwise wait for whole tiles).  M0 carries the LDS base;
-// no compiled code in these kernels uses M0.  The five wait states cover SGPR
-// operands written by VALU (readfirstlane) just before.
-__device__ __forceinline__ void copy16_to_lds(MLA_LDS char* lds_base, int voff, i32x4 desc,
-                                              int soff) {
-  const int m0 = uni((int)(size_t)lds_base);
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 4\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
-               :
-               : "s"(m0), "v"(voff), "s"(desc), "s"(soff)
-               : "memory", "m0");
-}
-
-// s_waitcnt between compiler fences: the wait intrinsic alone does not keep
-// the scheduler from moving LDS reads above it.
-template <int kImm>
-__device__ __forceinline__ void fenced_wait() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_waitcnt(kImm);
-  asm volatile("" ::: "memory");
-}
-
-// The page copy of PageLoader through copy16_to_lds.
-struct AsmPageLoader {
-  int off[9];
-  __device__ __forceinline__ void init(int lane) {
-#pragma unroll
-    for (int k = 0; k < 9; ++k) {
-      const int pc = 64 * k + lane;
-      const int t = pc / kChunksPerRow;
-      const int p = pc - t * kChunksPerRow;
-      off[k] = t * kRowBytes + 16 * (p ^ swz(t));
-    }
-  }
-  static __device__ __forceinline__ i32x4 desc(const char* page, int live) {
-    const int n = live < kPage ? live : kPage;
-    return buffer_desc(page, n * kRowBytes);
-  }
-  // copy i (0 .. 17): block wave + 4 (i / 9), load i % 9
-  __device__ __forceinline__ void issue_one(MLA_LDS char* tile, i32x4 d, int wave, int i) const {
-    const int base = (wave + 4 * (i / 9)) * 8 * kRowBytes;
-    copy16_to_lds(tile + base + 1024 * (i % 9), off[i % 9], d, base);
-  }
-};
-
-struct AsmPendingCopy {
-  MLA_LDS char* tile;
-  i32x4 desc;
-  bool valid;
-};
-
 // A page copy whose 18 per-wave instructions are spread over the k-steps of
 // a score product, so the wave never stalls on a long run of memory issues.
 struct PendingCopy {
