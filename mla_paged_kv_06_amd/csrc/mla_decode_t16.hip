@@ -1,0 +1,318 @@
+// Paged MLA decode for gfx950, workgroups of at most 16 query rows (the
+// memory-bound regime: few heads, one query token).
+//
+// What is computed, and the layouts shared with the other decode kernels,
+// are described in mla_decode.hip (FlashMLA release note: MLA principles and
+// the paged bf16 cache; DeepSeek-V3 summary: one latent shared by all heads).
+//
+// With 16 rows there is one row tile, so the four waves split the tokens:
+// wave w scores token tile w (tokens 16 w .. 16 w + 15) of every 64-token
+// page for all 16 rows (18 MFMA 16x16x32; every K byte of the page is read
+// from LDS once).  The four tile maxima of each row meet in LDS, so every
+// wave takes the same running max and the same rescale decision and applies
+// it to its own accumulators; each wave writes its bf16 weights into its
+// 8-byte half of the value product's B-operand slot, and then runs the value
+// product of its 128 output columns over the whole page (16 MFMA).  Each
+// wave sums its own tokens' weights; the four sums meet at the end.
+//
+// Page copies and their waits are those of the other 16/32-row kernel: the
+// page is double-buffered, the next page's 18 copies per wave go out one per
+// k-step of the score product, and the top of a page waits for this wave's
+// copies, then a barrier.
+
+#include "mla_decode_common.h"
+
+namespace mla {
+
+namespace t16 {
+constexpr int kKS = kD / 32;  // 18 k-steps of the score product
+constexpr int kCT = 8;        // 16-column tiles per wave (128 columns)
+}  // namespace t16
+
+__global__ void __launch_bounds__(kThreads, 1)
+    decode_kernel_t16(const DecodeParams prm, const uint16_t* __restrict__ q_ptr,
+                      const uint16_t* __restrict__ kv_ptr, const int32_t* __restrict__ block_table,
+                      const int32_t* __restrict__ seqlens, const int32_t* __restrict__ meta,
+                      const int32_t* __restrict__ splits, uint16_t* __restrict__ out_ptr,
+                      float* __restrict__ lse_ptr, float* __restrict__ o_acc,
+                      float* __restrict__ lse_acc) {
+  using namespace t16;
+  __shared__ __attribute__((aligned(1024))) char tile0_[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) char tile1_[kTileBytes];
+  __shared__ __attribute__((aligned(16))) bf16x8 pbuf[2][64];  // [32-token k-step][lane]
+  __shared__ float mx_buf[kWaves][16];                          // [wave][row]: tile max
+  __shared__ float stat_l[kWaves][16];                          // [wave][row]: weight sums
+  MLA_LDS char* tile0 = (MLA_LDS char*)tile0_;
+  MLA_LDS char* tile1 = (MLA_LDS char*)tile1_;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = uni(threadIdx.x >> 6);  // wave-uniform: SGPR offsets and M0
+  const int l16 = lane & 15;
+  const int g = lane >> 4;
+
+  // XCD-aware mapping: consecutive partitions go to different XCDs
+  const int bid = blockIdx.x;
+  const int part = (bid >> 3) * 8 + (bid & 7);
+  if (part >= prm.num_parts) return;
+
+  const int32_t* m = meta + part * kMetaInts;
+  const int eb = uni(m[2]), ej = uni(m[3]);
+  Item cur = {uni(m[0]), uni(m[1])};
+  if (!item_before(cur, eb, ej)) return;
+  int split_idx = uni(m[4]);
+
+  const int col_base = wave * (kDv / kWaves);
+  const bool row_live = l16 < prm.R;
+
+  // K fragment (A of the score product): token 16 wave + l16 of the page,
+  // logical chunk 4 ks + g at physical (4 ks + g) ^ (token & 7)
+  const int sw = l16 & 7;
+  const int k_lane = (16 * wave + l16) * kRowBytes + 16 * (g ^ (sw & 3));
+  const int k_even = k_lane + ((sw & 4) ? 64 : 0);
+  const int k_odd = k_lane - ((sw & 4) ? 64 : 0);
+  // V^T fragment (A of the value product) by transposed read
+  const int vt = 4 * g + (l16 >> 2);
+  const int vsw = swz(vt);
+  const int ve = (l16 & 3) >> 1;
+  int v_off[4];
+#pragma unroll
+  for (int c4 = 0; c4 < 4; ++c4)
+    v_off[c4] = vt * kRowBytes + 16 * ((2 * c4 + ve) ^ vsw) + 8 * (l16 & 1);
+
+  bf16x8 qf[kKS];
+  f32x4 o[kCT];  // O^T tiles: row l16, columns col_base + 16 ct + 4 g + r
+  float m_used = -INFINITY, l_part = 0.f;  // running max (raw units); own tokens' sum
+  int n_vis = 0;
+  int L = 0;
+  int seg_s_lo = 0, seg_nsplit = 0;
+
+  const char* kvbase = (const char*)kv_ptr;
+  PageLoader loader;
+  loader.init(lane);
+
+  auto begin_segment = [&](int b) __attribute__((always_inline)) {
+    L = uni(seqlens[b]);
+    seg_s_lo = uni(splits[b]);
+    seg_nsplit = uni(splits[b + 1]) - seg_s_lo;
+    // rows past R read row 0 and are never stored; they see no tokens
+    const uint16_t* qrow = q_ptr + ((size_t)b * prm.R + (row_live ? l16 : 0)) * kD + 8 * g;
+    static_for<0, kKS>([&](auto kc) __attribute__((always_inline)) {
+      qf[decltype(kc)::value] = *(const bf16x8*)(qrow + 32 * decltype(kc)::value);
+    });
+    const int i = (row_live ? l16 : 0) / prm.h_q;
+    int n = prm.causal ? (L - prm.s_q + 1 + i) : L;
+    n = n < 0 ? 0 : (n > L ? L : n);
+    n_vis = row_live ? n : 0;
+    m_used = -INFINITY;
+    l_part = 0.f;
+    static_for<0, kCT>([&](auto c) __attribute__((always_inline)) {
+      o[decltype(c)::value] = f32x4{0.f, 0.f, 0.f, 0.f};
+    });
+  };
+
+  auto load_item = [&](MLA_LDS char* tile, Item it) __attribute__((always_inline)) -> bool {
+    const int L_it = uni(seqlens[it.b]);
+    if (it.j * kPage >= L_it) return false;
+    const int phys = uni(block_table[(size_t)it.b * prm.max_pages + it.j]);
+    loader.issue(tile, kvbase + (size_t)phys * kTileBytes, L_it - it.j * kPage, wave);
+    return true;
+  };
+
+  auto next_copy = [&](MLA_LDS char* tile, Item it, bool has) __attribute__((always_inline)) {
+    PendingCopy cp;
+    cp.tile = tile;
+    cp.valid = false;
+    cp.rsrc = PageLoader::resource(kvbase, 0);
+    if (has) {
+      const int L_it = uni(seqlens[it.b]);
+      if (it.j * kPage < L_it) {
+        const int phys = uni(block_table[(size_t)it.b * prm.max_pages + it.j]);
+        cp.rsrc = PageLoader::resource(kvbase + (size_t)phys * kTileBytes, L_it - it.j * kPage);
+        cp.valid = true;
+      }
+    }
+    return cp;
+  };
+
+  // next item after `it` of the current sequence (whose length is L)
+  auto advance = [&](Item it) __attribute__((always_inline)) {
+    Item nx = it;
+    const int n_slots = (L + kPage - 1) / kPage;
+    if (it.j + 1 < (n_slots > 0 ? n_slots : 1)) {
+      nx.j = uni(it.j + 1);
+    } else {
+      nx.b = uni(it.b + 1);
+      nx.j = 0;
+    }
+    return nx;
+  };
+
+  // V^T fragment ct (16 columns x 32 tokens 32 kk ..) by transposed reads
+  auto load_v = [&](MLA_LDS char* tile, int kk, bf16x8& vf, int ct) __attribute__((always_inline)) {
+    const int cta = col_base / 16 + ct;
+    const int a = v_off[cta & 3] + 128 * (cta >> 2) + kk * 32 * kRowBytes;
+    i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MLA_LDS i16x4*)(tile + a));
+    i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MLA_LDS i16x4*)(tile + a + 16 * kRowBytes));
+    vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+
+  // One page: scores of this wave's token tile, max exchange, softmax,
+  // weights to LDS, value product of this wave's 128 columns.
+  auto compute_page = [&](MLA_LDS char* tile, int j, const PendingCopy& cp)
+                          __attribute__((always_inline)) {
+    f32x4 s = {0.f, 0.f, 0.f, 0.f};
+    auto load_k = [&](int ks) __attribute__((always_inline)) {
+      return *(MLA_LDS bf16x8*)(tile + ((ks & 1) ? k_odd : k_even) + 64 * ks);
+    };
+    constexpr int DK = 6;  // K fragments in flight ahead of their product
+    bf16x8 kr[DK + 1];
+    static_for<0, DK>([&](auto ic) __attribute__((always_inline)) {
+      kr[decltype(ic)::value] = load_k(decltype(ic)::value);
+    });
+    static_for<0, kKS>([&](auto ksc) __attribute__((always_inline)) {
+      constexpr int ks = decltype(ksc)::value;
+      if constexpr (ks + DK < kKS) kr[(ks + DK) % (DK + 1)] = load_k(ks + DK);
+      // the next page's 18 copy instructions, one per k-step
+      static_assert(kKS == kLoadsPerWave, "one copy per k-step");
+      if (cp.valid) loader.issue_one(cp.tile, cp.rsrc, wave, ks);
+      s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kr[ks % (DK + 1)], qf[ks], s, 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    });
+    // ---- tile max (raw score units; the scale is positive), shared
+    const int tok0 = j * kPage + 16 * wave + 4 * g;
+    float x[4];
+    float mt = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      x[r] = (tok0 + r < n_vis) ? s[r] : -INFINITY;
+      mt = fmaxf(mt, x[r]);
+    }
+    mt = wave_max_x4(mt);
+    if (g == 0) mx_buf[wave][l16] = mt;
+    // the first V^T fragments do not depend on the weights
+    constexpr int DV = 4;
+    bf16x8 vr[DV + 1];
+    static_for<0, DV>([&](auto ic) __attribute__((always_inline)) {
+      constexpr int u = decltype(ic)::value;  // fragment u: column tile u / 2, k-step u % 2
+      load_v(tile, u % 2, vr[u], u / 2);
+    });
+    lds_barrier();
+    const float mx = fmaxf(fmaxf(mx_buf[0][l16], mx_buf[1][l16]),
+                           fmaxf(mx_buf[2][l16], mx_buf[3][l16]));
+    // ---- online softmax (log2 domain): every wave sees the same mx and
+    //      m_used, so every wave takes the same decision
+    const bool upd = __builtin_amdgcn_ballot_w64((mx - m_used) * prm.scale_log2 >
+                                                 kRescaleThreshold) != 0;
+    const float mn = upd ? fmaxf(m_used, mx) : m_used;
+    const float alpha = (upd && mn != -INFINITY)
+                            ? __builtin_amdgcn_exp2f((m_used - mn) * prm.scale_log2)
+                            : 1.f;
+    m_used = mn;
+    l_part *= alpha;
+    const float nref = (mn == -INFINITY) ? 0.f : -mn * prm.scale_log2;
+    float p[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      p[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[r], prm.scale_log2, nref));
+      l_part += p[r];
+    }
+    // k-step kk = wave / 2 of the value product; k-slot 8g + 4 (wave & 1) + r
+    // <-> token 32 kk + 16 (wave & 1) + 4g + r: this wave's half of the slot
+    const bf16x2 a0 = to_bf16x2(p[0], p[1]);
+    const bf16x2 a1 = to_bf16x2(p[2], p[3]);
+    *(MLA_LDS bf16x4*)((MLA_LDS char*)&pbuf[wave >> 1][lane] + 8 * (wave & 1)) =
+        bf16x4{a0[0], a0[1], a1[0], a1[1]};
+    if (upd) {
+      static_for<0, kCT>([&](auto c) __attribute__((always_inline)) {
+        o[decltype(c)::value] *= alpha;
+      });
+    }
+    lds_barrier();
+    // ---- value product: all 16 rows, this wave's 128 columns, 64 tokens
+    const bf16x8 pb0 = pbuf[0][lane];
+    const bf16x8 pb1 = pbuf[1][lane];
+    static_for<0, 2 * kCT>([&](auto uc) __attribute__((always_inline)) {
+      constexpr int u = decltype(uc)::value;  // column tile u / 2, k-step u % 2
+      if constexpr (u + DV < 2 * kCT) load_v(tile, (u + DV) % 2, vr[(u + DV) % (DV + 1)], (u + DV) / 2);
+      o[u / 2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vr[u % (DV + 1)], (u % 2) ? pb1 : pb0,
+                                                         o[u / 2], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    });
+  };
+
+  auto finish_segment = [&](int b) __attribute__((always_inline)) {
+    const bool direct = seg_nsplit <= 1;
+    const int slot = seg_s_lo + split_idx;
+    const float lw = wave_sum_x4(l_part);
+    if (g == 0) stat_l[wave][l16] = lw;
+    lds_barrier();
+    const float lt = (stat_l[0][l16] + stat_l[1][l16]) + (stat_l[2][l16] + stat_l[3][l16]);
+    const float inv = lt > 0.f ? 1.f / lt : 0.f;
+    if (row_live) {
+      if (wave == 0 && g == 0) {
+        const float lse2 = lt > 0.f ? m_used * prm.scale_log2 + __builtin_amdgcn_logf(lt) : -INFINITY;
+        if (direct)
+          lse_ptr[(size_t)b * prm.R + l16] = lse2 * kLn2;
+        else
+          lse_acc[(size_t)slot * prm.R + l16] = lse2;
+      }
+      if (direct) {
+        uint16_t* orow = out_ptr + ((size_t)b * prm.R + l16) * kDv + col_base + 4 * g;
+        static_for<0, kCT>([&](auto cc) __attribute__((always_inline)) {
+          constexpr int ct = decltype(cc)::value;
+          const f32x4 v = o[ct] * inv;
+          const bf16x2 a = to_bf16x2(v[0], v[1]);
+          const bf16x2 c = to_bf16x2(v[2], v[3]);
+          *(bf16x4*)(orow + 16 * ct) = bf16x4{a[0], a[1], c[0], c[1]};
+        });
+      } else {
+        float* orow = o_acc + ((size_t)slot * prm.R + l16) * kDv + col_base + 4 * g;
+        static_for<0, kCT>([&](auto cc) __attribute__((always_inline)) {
+          constexpr int ct = decltype(cc)::value;
+          *(f32x4*)(orow + 16 * ct) = o[ct] * inv;
+        });
+      }
+    }
+    split_idx = 0;  // later sequences of this partition start at their page 0
+  };
+
+  // One step: compute `cur` from tile A while the next page streams into B.
+  auto step = [&](MLA_LDS char* tA, MLA_LDS char* tB) __attribute__((always_inline)) -> bool {
+    const Item nx = advance(cur);
+    const bool has_next = item_before(nx, eb, ej);
+    // descriptor of the next copy first: its scalar loads (block table and
+    // lengths, never written here) overlap the wait below
+    PendingCopy cp = next_copy(tB, nx, has_next);
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);  // this wave's part of tile A landed
+    __syncthreads();                       // ... and every wave's; B is free
+    if (cur.j * kPage < L) {
+      compute_page(tA, cur.j, cp);
+    } else if (cp.valid) {
+      for (int i = 0; i < kLoadsPerWave; ++i) loader.issue_one(cp.tile, cp.rsrc, wave, i);
+    }
+    if (!has_next || nx.b != cur.b) {
+      finish_segment(cur.b);
+      if (has_next) begin_segment(nx.b);
+    }
+    cur = nx;
+    return has_next;
+  };
+
+  begin_segment(cur.b);
+  load_item(tile0, cur);
+  while (true) {
+    if (!step(tile0, tile1)) break;
+    if (!step(tile1, tile0)) break;
+  }
+}
+
+}  // namespace mla
+
+extern "C" hipError_t mla_launch_decode_t16(const mla::DecodeParams* prm, hipStream_t stream) {
+  using namespace mla;
+  const int groups = (prm->num_parts + 7) / 8;
+  hipLaunchKernelGGL(decode_kernel_t16, dim3(groups * 8), dim3(kThreads), 0, stream, *prm, prm->q,
+                     prm->kv, prm->block_table, prm->seqlens, prm->meta, prm->splits, prm->out,
+                     prm->lse, prm->o_acc, prm->lse_acc);
+  return hipGetLastError();
+}
