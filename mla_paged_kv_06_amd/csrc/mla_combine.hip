@@ -8,27 +8,44 @@
 namespace mla {
 
 // Combine: merge split partials by log-sum-exp.  One wave per query row
-// (4 rows per workgroup), 8 output columns per lane.  The weights of all
-// splits are computed first (lanes over splits, a wave max and sum), kept in
-// LDS, and the partial rows are then read with several loads in flight.
+// (4 rows per workgroup), 8 output columns per lane.  The partial rows of the
+// first kCombineUnroll splits are requested before anything else, so their
+// loads overlap those of the split lse values; the weights of splits below
+// 64 are then broadcast from the lane that computed them.
 constexpr int kCombineRows = 4;
-constexpr int kCombineChunk = 1024;  // splits whose weights sit in LDS at once
+constexpr int kCombineUnroll = 8;  // partial rows in flight per lane
+
+__device__ __forceinline__ float lane_value(float v, int lane) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
+}
 
 __global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ o_acc,
                                                       const float* __restrict__ lse_acc,
                                                       const int32_t* __restrict__ splits, int R,
                                                       uint16_t* __restrict__ out,
                                                       float* __restrict__ lse) {
-  __shared__ float s_w[kCombineRows][kCombineChunk];
+  constexpr int U = kCombineUnroll;
   const int b = blockIdx.y;
   const int wv = threadIdx.x >> 6;
   const int row = blockIdx.x * kCombineRows + wv;
   const int t = threadIdx.x & 63;
-  const int s0 = splits[b];
-  const int ns = splits[b + 1] - s0;
+  const int s0 = __builtin_amdgcn_readfirstlane(splits[b]);
+  const int ns = __builtin_amdgcn_readfirstlane(splits[b + 1]) - s0;
   if (ns <= 1 || row >= R) return;  // uniform per wave; no block barrier below
   const float* lrow = lse_acc + (size_t)s0 * R + row;
-  // the first 64 splits' lse sit in one register per lane (one load round)
+  const float* orow_acc = o_acc + ((size_t)s0 * R + row) * kDv + 8 * t;
+  f32x4 v[2 * U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    if (u < ns) {
+      const float* src = orow_acc + (size_t)u * R * kDv;
+      v[2 * u] = *(const f32x4*)src;
+      v[2 * u + 1] = *(const f32x4*)(src + 4);
+    } else {
+      v[2 * u] = v[2 * u + 1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  }
+  // split weights: lanes over splits, a wave max and sum
   const float l0 = t < ns ? lrow[(size_t)t * R] : -INFINITY;
   float mx = l0;
   for (int s = t + 64; s < ns; s += 64) mx = fmaxf(mx, lrow[(size_t)s * R]);
@@ -40,44 +57,42 @@ __global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ 
     if (t == 0) lse[(size_t)b * R + row] = -INFINITY;
     return;
   }
-  const float w0 = __builtin_amdgcn_exp2f(l0 - mx);  // -inf -> 0
-  float z = w0;
+  const float e0 = __builtin_amdgcn_exp2f(l0 - mx);  // -inf -> 0
+  float z = e0;
   for (int s = t + 64; s < ns; s += 64) z += __builtin_amdgcn_exp2f(lrow[(size_t)s * R] - mx);
 #pragma unroll
   for (int d = 32; d >= 1; d >>= 1) z += __shfl_xor(z, d);
   const float inv = 1.f / z;
+  const float w0 = e0 * inv;  // weight of split t (t < 64)
+  auto weight = [&](int si) __attribute__((always_inline)) {
+    return si < 64 ? lane_value(w0, si) : __builtin_amdgcn_exp2f(lrow[(size_t)si * R] - mx) * inv;
+  };
   f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0;
-  const float* orow_acc = o_acc + ((size_t)s0 * R + row) * kDv + 8 * t;
-  constexpr int U = 8;  // partial rows in flight per lane
-  for (int c0 = 0; c0 < ns; c0 += kCombineChunk) {
-    const int nc = ns - c0 < kCombineChunk ? ns - c0 : kCombineChunk;
-    if (c0 == 0 && t < nc) s_w[wv][t] = w0 * inv;
-    for (int s = (c0 == 0 ? t + 64 : t); s < nc; s += 64)
-      s_w[wv][s] = __builtin_amdgcn_exp2f(lrow[(size_t)(c0 + s) * R] - mx) * inv;
-    __builtin_amdgcn_wave_barrier();
-    int s = 0;
-    for (; s + U <= nc; s += U) {
-      f32x4 v[2 * U];
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const float* src = orow_acc + (size_t)(c0 + s + u) * R * kDv;
+  for (int u = 0; u < U; ++u) {
+    if (u < ns) {
+      const float w = weight(u);
+      a0 += w * v[2 * u];
+      a1 += w * v[2 * u + 1];
+    }
+  }
+  for (int s = U; s < ns; s += U) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (s + u < ns) {
+        const float* src = orow_acc + (size_t)(s + u) * R * kDv;
         v[2 * u] = *(const f32x4*)src;
         v[2 * u + 1] = *(const f32x4*)(src + 4);
       }
+    }
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const float w = s_w[wv][s + u];
+    for (int u = 0; u < U; ++u) {
+      if (s + u < ns) {
+        const float w = weight(s + u);
         a0 += w * v[2 * u];
         a1 += w * v[2 * u + 1];
       }
     }
-    for (; s < nc; ++s) {
-      const float* src = orow_acc + (size_t)(c0 + s) * R * kDv;
-      const float w = s_w[wv][s];
-      a0 += w * *(const f32x4*)src;
-      a1 += w * *(const f32x4*)(src + 4);
-    }
-    __builtin_amdgcn_wave_barrier();
   }
   bf16x2 r0 = to_bf16x2(a0[0], a0[1]);
   bf16x2 r1 = to_bf16x2(a0[2], a0[3]);
@@ -108,10 +123,26 @@ __global__ void __launch_bounds__(256) combine_wide_kernel(const float* __restri
   const int ns = __builtin_amdgcn_readfirstlane(splits[b + 1]) - s0;
   if (ns <= 1) return;  // uniform over the workgroup
   const float* lrow = lse_acc + (size_t)s0 * R + row;
+  const float* base = o_acc + ((size_t)s0 * R + row) * kDv + 8 * t;
+  // this wave's first kWideUnroll partial rows (splits wv, wv + 4, ...) are
+  // requested first: their loads overlap those of the lse values
+  f32x4 v[2 * kWideUnroll];
+#pragma unroll
+  for (int u = 0; u < kWideUnroll; ++u) {
+    const int si = wv + kWaves * u;
+    if (si < ns) {
+      const float* src = base + (size_t)si * R * kDv;
+      v[2 * u] = *(const f32x4*)src;
+      v[2 * u + 1] = *(const f32x4*)(src + 4);
+    } else {
+      v[2 * u] = v[2 * u + 1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  }
   // max and sum of the split weights (lanes over splits; every wave computes
   // the same values)
-  float mx = -INFINITY;
-  for (int s = t; s < ns; s += 64) mx = fmaxf(mx, lrow[(size_t)s * R]);
+  const float l0 = t < ns ? lrow[(size_t)t * R] : -INFINITY;
+  float mx = l0;
+  for (int s = t + 64; s < ns; s += 64) mx = fmaxf(mx, lrow[(size_t)s * R]);
 #pragma unroll
   for (int d = 32; d >= 1; d >>= 1) mx = fmaxf(mx, __shfl_xor(mx, d));
   uint16_t* orow = out + ((size_t)b * R + row) * kDv;
@@ -122,34 +153,37 @@ __global__ void __launch_bounds__(256) combine_wide_kernel(const float* __restri
     }
     return;
   }
-  float z = 0.f;
-  for (int s = t; s < ns; s += 64) z += __builtin_amdgcn_exp2f(lrow[(size_t)s * R] - mx);
+  const float e0 = __builtin_amdgcn_exp2f(l0 - mx);
+  float z = e0;
+  for (int s = t + 64; s < ns; s += 64) z += __builtin_amdgcn_exp2f(lrow[(size_t)s * R] - mx);
 #pragma unroll
   for (int d = 32; d >= 1; d >>= 1) z += __shfl_xor(z, d);
   const float inv = 1.f / z;
-  // this wave's splits: wv, wv + 4, ...
+  const float w0 = e0 * inv;  // weight of split t (t < 64)
+  auto weight = [&](int si) __attribute__((always_inline)) {
+    return si < 64 ? lane_value(w0, si) : __builtin_amdgcn_exp2f(lrow[(size_t)si * R] - mx) * inv;
+  };
   f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0;
-  const float* base = o_acc + ((size_t)s0 * R + row) * kDv + 8 * t;
   for (int s = wv; s < ns; s += kWaves * kWideUnroll) {
-    f32x4 v[2 * kWideUnroll];
-    float w[kWideUnroll];
+    if (s != wv) {
 #pragma unroll
-    for (int u = 0; u < kWideUnroll; ++u) {
-      const int si = s + kWaves * u;
-      if (si < ns) {
-        const float* src = base + (size_t)si * R * kDv;
-        v[2 * u] = *(const f32x4*)src;
-        v[2 * u + 1] = *(const f32x4*)(src + 4);
-        w[u] = __builtin_amdgcn_exp2f(lrow[(size_t)si * R] - mx) * inv;
-      } else {
-        v[2 * u] = v[2 * u + 1] = f32x4{0.f, 0.f, 0.f, 0.f};
-        w[u] = 0.f;
+      for (int u = 0; u < kWideUnroll; ++u) {
+        const int si = s + kWaves * u;
+        if (si < ns) {
+          const float* src = base + (size_t)si * R * kDv;
+          v[2 * u] = *(const f32x4*)src;
+          v[2 * u + 1] = *(const f32x4*)(src + 4);
+        }
       }
     }
 #pragma unroll
     for (int u = 0; u < kWideUnroll; ++u) {
-      a0 += w[u] * v[2 * u];
-      a1 += w[u] * v[2 * u + 1];
+      const int si = s + kWaves * u;
+      if (si < ns) {
+        const float w = weight(si);
+        a0 += w * v[2 * u];
+        a1 += w * v[2 * u + 1];
+      }
     }
   }
   s_acc[wv][0][t] = a0;
