@@ -120,6 +120,37 @@ def test_edge_lengths(mla, h_q, s_q, causal):
     compare(out, lse, ref_out, ref_lse)
 
 
+@pytest.mark.parametrize("s_q,h_q,causal", [(1, 8, False), (1, 20, False), (5, 7, True),
+                                             (3, 40, True), (4, 128, True), (16, 128, True)])
+def test_row_shapes(mla, s_q, h_q, causal):
+    """Row counts R = s_q * h_q that are not multiples of 16 (partial row tiles
+    in every kernel variant), several row groups, and the largest supported R
+    (2048 rows: 32 row groups of 64)."""
+    _say(f"[parity] rows s_q={s_q} h_q={h_q} causal={causal}")
+    case = make_case([1, 100, 700, 65, 0, 130], s_q, h_q, causal, seed=31 + s_q * h_q,
+                     pool_factor=1.25, poison_unused=True, poison_tail=True)
+    out, lse = run(mla, case)
+    ref_out, ref_lse = oracle.decode_ref(case)
+    compare(out, lse, ref_out, ref_lse)
+
+
+@pytest.mark.parametrize("h_q", [16, 64])
+def test_many_short_sequences(mla, h_q):
+    """1100 short sequences: the chunked scheduler path, many sequences per
+    partition, and both combine kernels; sampled against the oracle."""
+    _say(f"[parity] 1100 short sequences h_q={h_q}")
+    rng = np.random.Generator(np.random.PCG64(97 + h_q))
+    L = [int(x) for x in rng.integers(0, 300, size=1100)]
+    L[5] = 0
+    L[17] = 4000
+    case = make_case(L, 1, h_q, False, seed=37 + h_q, pool_factor=1.1,
+                     poison_unused=True, poison_tail=True)
+    out, lse = run(mla, case)
+    pick = sorted({0, 5, 17, 511, 512, 1023, 1024, 1099} | {int(x) for x in rng.integers(0, 1100, 12)})
+    ref_out, ref_lse = oracle.decode_ref(case, batches=pick)
+    compare(out, lse, ref_out, ref_lse, batches=pick)
+
+
 @pytest.mark.parametrize("num_cus", [1, 3, 64, 256, 1024])
 def test_forced_partition_counts(mla, num_cus):
     _say(f"[parity] num_cus={num_cus}")
