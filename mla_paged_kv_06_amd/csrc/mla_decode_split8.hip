@@ -26,9 +26,10 @@
 // buffer loads into LDS, resource bounded by the live tokens).  A CU moves
 // only about 50 B/clk into LDS, so a page costs about 1,500 cycles of copy
 // time, and a wave whose copy instruction finds the queue full stalls; the
-// next page's nine copies are therefore spread over the whole current page,
-// one every six or seven matrix instructions.  The top of a page waits for
-// this wave's copies, then a barrier.
+// next page's nine copies are therefore spread over the first half of the
+// current page, one every four matrix instructions, which leaves the second
+// half for them to land.  The top of a page waits for this wave's copies,
+// then a barrier.
 
 #include "mla_decode_common.h"
 
@@ -215,11 +216,11 @@ __global__ void __launch_bounds__(s8::kThreads8, 1)
     static_for<0, kKS>([&](auto ksc) __attribute__((always_inline)) {
       constexpr int ks = decltype(ksc)::value;
       if constexpr (ks + DK < kKS) kr[(ks + DK) % (DK + 1)] = load_k(ks + DK);
-      // the next page's nine copies are spread over the whole page: k-steps
-      // 0, 6, 12 of each score product and column tiles 1, 3 (half 0) or 1
-      // (half 1) of the value products
-      if constexpr (ks % 6 == 0)
-        if (cp.valid) issue_copy(cp.tile, cp.rsrc, 5 * h + ks / 6);
+      // the next page's nine copies go out during the first half page:
+      // k-steps 0, 4, 8, 12, 16 of its score product and the first four
+      // column tiles of its value product
+      if constexpr (h == 0 && ks % 4 == 0)
+        if (cp.valid) issue_copy(cp.tile, cp.rsrc, ks / 4);
       s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kr[ks % (DK + 1)], qf[ks], s, 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
     });
@@ -288,10 +289,8 @@ __global__ void __launch_bounds__(s8::kThreads8, 1)
     static_for<0, kCT>([&](auto ctc) __attribute__((always_inline)) {
       constexpr int ct = decltype(ctc)::value;
       if constexpr (ct + DV < kCT) load_v(tile, h, vr[(ct + DV) % (DV + 1)], ct + DV);
-      if constexpr (h == 0 && (ct == 1 || ct == 3))
-        if (cp.valid) issue_copy(cp.tile, cp.rsrc, 3 + ct / 2);
-      if constexpr (h == 1 && ct == 1)
-        if (cp.valid) issue_copy(cp.tile, cp.rsrc, 8);
+      if constexpr (h == 0 && ct < 4)
+        if (cp.valid) issue_copy(cp.tile, cp.rsrc, 5 + ct);
       static_for<0, kRT>([&](auto rc) __attribute__((always_inline)) {
         constexpr int r2 = decltype(rc)::value;
         o[r2][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vr[ct % (DV + 1)], pb[r2], o[r2][ct],
