@@ -76,7 +76,7 @@ size_t ws_bytes(int batch, int R, int parts) {
 
 extern "C" hipError_t mla_launch_decode(const mla::DecodeParams* prm, int rows_variant,
                                         hipStream_t stream);
-extern "C" hipError_t mla_launch_decode_split8(const mla::DecodeParams* prm, hipStream_t stream);
+extern "C" hipError_t mla_launch_decode_sv64(const mla::DecodeParams* prm, hipStream_t stream);
 extern "C" hipError_t mla_launch_decode_t16(const mla::DecodeParams* prm, hipStream_t stream);
 extern "C" hipError_t mla_launch_combine(const float* o_acc, const float* lse_acc,
                                          const int32_t* splits, int batch, int R, uint16_t* out,
@@ -153,7 +153,7 @@ mla_status_t mla_decode_paged(const void* q, const void* kv_cache, const int32_t
   prm.causal = causal ? 1 : 0;
   prm.scale_log2 = (float)((double)softmax_scale * 1.4426950408889634);
   const int variant = rows_variant_of(R);
-  hipError_t e = variant == 64   ? mla_launch_decode_split8(&prm, stream)
+  hipError_t e = variant == 64   ? mla_launch_decode_sv64(&prm, stream)
                  : variant == 16 ? mla_launch_decode_t16(&prm, stream)
                                  : mla_launch_decode(&prm, variant, stream);
   return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
