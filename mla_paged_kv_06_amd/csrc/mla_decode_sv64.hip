@@ -338,8 +338,9 @@ __global__ void __launch_bounds__(sv::kThreadsSV, 1)
       vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
     };
 
-    // value product of one slot, with the nine copies of another spread
-    // over its column tiles
+    // value product of one slot; the nine copies of another go out first,
+    // right after the barrier: the earlier they leave, the less of their
+    // HBM latency is left to wait for two steps later
     auto value_slot = [&](MLA_LDS char* buf, int pb, MLA_LDS char* cbuf, i32x4 crs, bool cvalid)
                           __attribute__((always_inline)) {
       bf16x8 pw[kRT];
@@ -350,6 +351,10 @@ __global__ void __launch_bounds__(sv::kThreadsSV, 1)
         pw[r2] = pbuf[pb][r2][lane];
         al[r2] = alpha_buf[pb][16 * r2 + l16];
         resc |= al[r2] != 1.f;
+      }
+      if (cvalid) {
+#pragma unroll
+        for (int k = 0; k < kCopies; ++k) copy_one(cbuf, crs, k);
       }
       constexpr int DV = 3;
       bf16x8 vr[DV + 1];
@@ -367,11 +372,6 @@ __global__ void __launch_bounds__(sv::kThreadsSV, 1)
       static_for<0, kCT>([&](auto ctc) __attribute__((always_inline)) {
         constexpr int ct = decltype(ctc)::value;
         if constexpr (ct + DV < kCT) load_v(buf, vr[(ct + DV) % (DV + 1)], ct + DV);
-        // copies k = 0 .. 8: two at column tile 0, then one per tile
-        if (cvalid) {
-          if constexpr (ct == 0) copy_one(cbuf, crs, 0);
-          copy_one(cbuf, crs, ct + 1);
-        }
         static_for<0, kRT>([&](auto rc) __attribute__((always_inline)) {
           constexpr int r2 = decltype(rc)::value;
           o[r2][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vr[ct % (DV + 1)], pw[r2],
