@@ -147,6 +147,67 @@ def measured_traffic(workload):
     return int(w["fetch_bytes"] + w["write_bytes"])
 
 
+def absorption_rates(mla, b, s_q, h_q, seed, dev, launches_per_rep=None):
+    """Time the query and output absorption products (the row next to the
+    decode) on this workload's token and head counts, synthetic weights; each
+    launch reads a different replica (more than 1 GiB in all) so that no
+    weight is served from the 256 MB last-level cache.  Returns per product:
+    average launch time (HIP events around a graph of back-to-back launches
+    on the launch stream), algorithmic bytes and flops per launch, and the
+    fraction of the HBM peak (both products are weight/activation streams at
+    2 flops per weight byte per token)."""
+    import torch
+    from workloads import make_absorb_case
+
+    case = make_absorb_case(b, s_q, h_q, seed)
+
+    def up(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(
+            torch.bfloat16)
+
+    M = b * s_q
+    qb = h_q * 512 * 128 * 2 + M * h_q * (128 + 64 + 576) * 2
+    ob = h_q * 128 * 512 * 2 + M * h_q * (512 + 128) * 2
+    fl = 2 * M * h_q * 128 * 512
+    R = max(2, math.ceil((1 << 30) / (qb + ob)))
+    base = [up(case.q_nope), up(case.q_rope), up(case.w_uk_t), up(case.lat_out), up(case.w_uv)]
+    reps = [base] + [[t.clone() for t in base] for _ in range(R - 1)]
+    q_out = [torch.empty((b, s_q, h_q, 576), dtype=torch.bfloat16, device=dev) for _ in range(R)]
+    o = [torch.empty((b, s_q, h_q, 128), dtype=torch.bfloat16, device=dev) for _ in range(R)]
+    out = {}
+    for name, fn, nb in (
+            ("query", lambda r: mla.absorb_query(reps[r][0], reps[r][1], reps[r][2], q_out[r]), qb),
+            ("output", lambda r: mla.absorb_output(reps[r][3], reps[r][4], o[r]), ob)):
+        for r in range(R):
+            fn(r)
+        torch.cuda.synchronize()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            for r in range(R):
+                fn(r)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        times = []
+        for _ in range(5):
+            e0.record()
+            g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1) / R)
+        ms = float(np.mean(times))
+        gbs = nb / (ms * 1e-3) / 1e9
+        out[name] = {"us": round(ms * 1e3, 3), "bytes": nb, "flops": fl,
+                     "GB_per_s": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+                     "TFLOP_per_s": round(fl / (ms * 1e-3) / 1e12, 2)}
+    out["replicas"] = R
+    return out
+
+
 def copy_calibration(mib, launches=5):
     """Plain device-to-device copies of a known size, for scaling the HBM byte
     counters (run under rocprofv3 --pmc)."""
@@ -171,6 +232,8 @@ def main():
     ap.add_argument("--replicas", type=int, default=0, help="0 = enough to exceed 1 GiB")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--no-next-rows", action="store_true",
+                    help="skip timing the absorption products next to the decode")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run plain device copies of MIB MiB (counter calibration)")
     args = ap.parse_args()
@@ -322,6 +385,17 @@ def main():
 
     value = nbytes / (ms_per_step * 1e-3) / 1e9
     achieved = nbytes / (dec_avg_ms * 1e-3) / 1e9
+    dec_tflops = flops / (dec_avg_ms * 1e-3) / 1e12
+    # the bound of the decode kernel: its arithmetic intensity against the
+    # ridge of the two peaks
+    mfma_bound = flops / nbytes > BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+    if mfma_bound:
+        roofline = {"bound": "mfma", "achieved": round(dec_tflops, 2), "peak": BF16_PEAK_TFLOPS,
+                    "unit": "TFLOP/s", "frac": round(dec_tflops / BF16_PEAK_TFLOPS, 4)}
+    else:
+        roofline = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                    "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4)}
+    roofline["traffic"] = measured_traffic(WORKLOAD_NAMES[k])
     res = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -342,19 +416,16 @@ def main():
             "causal": bool(case.causal), "seed": 1000 + k, "replicas": R,
             "timing": timing, "decode_launches_timed": n_rep * R,
         },
+        "algorithmic": {"bytes_per_step": int(nbytes), "flops_per_step": int(flops)},
         "tflops": round(flops / (ms_per_step * 1e-3) / 1e12, 3),
         "decode_kernel_ms": round(dec_avg_ms, 5),
         "decode_tflops": round(flops / (dec_avg_ms * 1e-3) / 1e12, 3),
-        "roofline": {
-            "bound": "hbm",
-            "achieved": round(achieved, 2),
-            "peak": HBM_PEAK_GBS,
-            "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": measured_traffic(WORKLOAD_NAMES[k]),
-        },
-        "mfma_frac": round(flops / (dec_avg_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+        "roofline": roofline,
+        "hbm_frac": round(achieved / HBM_PEAK_GBS, 4),
+        "mfma_frac": round(dec_tflops / BF16_PEAK_TFLOPS, 4),
     }
+    if not args.no_next_rows:
+        res["next_rows"] = {"absorption": absorption_rates(mla, b, s_q, h_q, 2000 + k, dev)}
     if not args.no_cpu_baseline:
         print("# timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(case)

@@ -81,6 +81,8 @@ typedef enum {
 #define MLA_MAX_BATCH 65536
 #define MLA_MAX_ROWS 2048    /* s_q * h_q */
 #define MLA_MAX_PARTS 4096   /* partitions of the key range (see below) */
+#define MLA_NOPE_DIM 128     /* per-head query part before absorption; value head width */
+#define MLA_ROPE_DIM 64      /* rotary part of the query and of the cache entry */
 
 /*
  * Number of key-range partitions used for `num_cus` compute units
@@ -147,6 +149,44 @@ mla_status_t mla_decode_paged(const void* q, const void* kv_cache, const int32_t
 mla_status_t mla_combine(const void* workspace, size_t workspace_bytes, const int32_t* num_splits,
                          int32_t batch, int32_t s_q, int32_t h_q, int32_t num_cus, void* out,
                          float* lse, hipStream_t stream);
+
+/*
+ * Query absorption, the step before mla_decode_paged.  Keys and values are
+ * one compressed latent per token, widened per head only at compute time
+ * (FlashMLA release note, paragraph on the MLA core principles; DeepSeek-V3
+ * summary, paragraph on memory efficiency).  Head h's key for token t is
+ * [W_UK,h c_t ; r_t] (c_t the 512-value latent, r_t the 64-value rotary key,
+ * W_UK,h a 128 x 512 matrix), so its score with the query [q_nope ; q_rope]
+ * equals the score of the absorbed query [W_UK,h^T q_nope ; q_rope] with the
+ * cached [c_t ; r_t].  For every query token m = b * s_q + i and head h:
+ *   q_out[m][h][0:512]   = W_UK,h^T q_nope[m][h]   (sum over 128 values)
+ *   q_out[m][h][512:576] = q_rope[m][h]            (copied)
+ *   q_nope  bf16 [batch][s_q][h_q][128]
+ *   q_rope  bf16 [batch][s_q][h_q][64]
+ *   w_uk_t  bf16 [h_q][512][128]: W_UK,h transposed, entry [h][c][d] = W_UK,h[d][c]
+ *   q_out   bf16 [batch][s_q][h_q][576]: the q of mla_decode_paged
+ * Products accumulate in fp32 and round once to bf16 (nearest even).  Device
+ * pointers, 16-byte aligned, caller-owned; asynchronous on `stream`; the call
+ * allocates nothing.  Errors: MLA_ERR_INVALID_ARGUMENT (null or misaligned
+ * pointer, non-positive size), MLA_ERR_UNSUPPORTED (batch > MLA_MAX_BATCH or
+ * s_q * h_q > MLA_MAX_ROWS), MLA_ERR_HIP.
+ */
+mla_status_t mla_absorb_query(const void* q_nope, const void* q_rope, const void* w_uk_t,
+                              int32_t batch, int32_t s_q, int32_t h_q, void* q_out,
+                              hipStream_t stream);
+
+/*
+ * Output absorption, the step after mla_decode_paged / mla_combine (same
+ * passages): head h's value for token t is W_UV,h c_t, so its output is
+ * W_UV,h applied to the latent output the decode returns.
+ *   o[m][h][:] = W_UV,h out[m][h][:]                (128 values from 512)
+ *   out   bf16 [batch][s_q][h_q][512]: the out of mla_decode_paged
+ *   w_uv  bf16 [h_q][128][512]: W_UV,h as stored, entry [h][d][c]
+ *   o     bf16 [batch][s_q][h_q][128]
+ * Accumulation, pointers, errors: as mla_absorb_query.
+ */
+mla_status_t mla_absorb_output(const void* out, const void* w_uv, int32_t batch, int32_t s_q,
+                               int32_t h_q, void* o, hipStream_t stream);
 
 /* Static, human-readable text of a status code. */
 const char* mla_status_string(mla_status_t status);

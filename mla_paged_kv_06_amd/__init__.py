@@ -29,12 +29,18 @@ __all__ = [
     "decode_paged",
     "combine",
     "mla_decode",
+    "NOPE_DIM",
+    "ROPE_DIM",
+    "absorb_query",
+    "absorb_output",
 ]
 
 HEAD_DIM = 576
 V_DIM = 512
 PAGE_SIZE = 64
 META_INTS = 8
+NOPE_DIM = 128  # per-head query part before absorption; value head width
+ROPE_DIM = 64
 
 _PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 _LIB_NAME = "libmla_paged.so"
@@ -78,6 +84,10 @@ def load_library() -> ctypes.CDLL:
     lib.mla_decode_paged.restype = ctypes.c_int
     lib.mla_combine.argtypes = [vp, sz, vp, i32, i32, i32, i32, vp, vp, vp]
     lib.mla_combine.restype = ctypes.c_int
+    lib.mla_absorb_query.argtypes = [vp, vp, vp, i32, i32, i32, vp, vp]
+    lib.mla_absorb_query.restype = ctypes.c_int
+    lib.mla_absorb_output.argtypes = [vp, vp, i32, i32, i32, vp, vp]
+    lib.mla_absorb_output.restype = ctypes.c_int
     lib.mla_status_string.argtypes = [ctypes.c_int]
     lib.mla_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -188,3 +198,40 @@ def mla_decode(q, kv_cache, block_table, cache_seqlens, softmax_scale, causal, n
                                 meta, splits, num_cus, stream=stream)
     combine(ws, splits, batch, s_q, h_q, out, lse, num_cus, stream)
     return out, lse
+
+
+def absorb_query(q_nope: torch.Tensor, q_rope: torch.Tensor, w_uk_t: torch.Tensor,
+                 q_out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Absorbed query ``[W_UK,h^T q_nope ; q_rope]`` per head: ``q_nope [b,s_q,h,128]``,
+    ``q_rope [b,s_q,h,64]``, ``w_uk_t [h,512,128]`` -> ``q_out [b,s_q,h,576]``."""
+    _need(q_nope, "q_nope", torch.bfloat16, 4)
+    _need(q_rope, "q_rope", torch.bfloat16, 4)
+    _need(w_uk_t, "w_uk_t", torch.bfloat16, 3)
+    batch, s_q, h_q, d = q_nope.shape
+    if d != NOPE_DIM or tuple(q_rope.shape) != (batch, s_q, h_q, ROPE_DIM):
+        raise ValueError("q_nope must be [b,s_q,h_q,128] and q_rope [b,s_q,h_q,64]")
+    if tuple(w_uk_t.shape) != (h_q, V_DIM, NOPE_DIM):
+        raise ValueError("w_uk_t must be [h_q,512,128]")
+    if q_out is None:
+        q_out = torch.empty((batch, s_q, h_q, HEAD_DIM), dtype=torch.bfloat16, device=q_nope.device)
+    _need(q_out, "q_out", torch.bfloat16, 4)
+    _check("mla_absorb_query", load_library().mla_absorb_query(
+        _ptr(q_nope), _ptr(q_rope), _ptr(w_uk_t), batch, s_q, h_q, _ptr(q_out), _stream(stream)))
+    return q_out
+
+
+def absorb_output(out: torch.Tensor, w_uv: torch.Tensor, o: Optional[torch.Tensor] = None,
+                  stream=None) -> torch.Tensor:
+    """Per-head output ``W_UV,h out``: ``out [b,s_q,h,512]``, ``w_uv [h,128,512]`` ->
+    ``o [b,s_q,h,128]``."""
+    _need(out, "out", torch.bfloat16, 4)
+    _need(w_uv, "w_uv", torch.bfloat16, 3)
+    batch, s_q, h_q, d = out.shape
+    if d != V_DIM or tuple(w_uv.shape) != (h_q, NOPE_DIM, V_DIM):
+        raise ValueError("out must be [b,s_q,h_q,512] and w_uv [h_q,128,512]")
+    if o is None:
+        o = torch.empty((batch, s_q, h_q, NOPE_DIM), dtype=torch.bfloat16, device=out.device)
+    _need(o, "o", torch.bfloat16, 4)
+    _check("mla_absorb_output", load_library().mla_absorb_output(
+        _ptr(out), _ptr(w_uv), batch, s_q, h_q, _ptr(o), _stream(stream)))
+    return o

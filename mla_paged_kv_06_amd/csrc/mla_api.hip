@@ -82,6 +82,12 @@ extern "C" hipError_t mla_launch_combine(const float* o_acc, const float* lse_ac
                                          const int32_t* splits, int batch, int R, uint16_t* out,
                                          float* lse, int wide, hipStream_t stream);
 
+extern "C" hipError_t mla_launch_absorb_query(const uint16_t* q_c, const uint16_t* q_r,
+                                              const uint16_t* w_uk_t, int M, int H,
+                                              uint16_t* q_out, hipStream_t stream);
+extern "C" hipError_t mla_launch_absorb_output(const uint16_t* lat_out, const uint16_t* w_uv,
+                                               int M, int H, uint16_t* o, hipStream_t stream);
+
 extern "C" {
 
 int32_t mla_num_partitions(int32_t s_q, int32_t h_q, int32_t num_cus) {
@@ -176,6 +182,38 @@ mla_status_t mla_combine(const void* workspace, size_t workspace_bytes, const in
   const int wide = parts >= 8 * batch ? 1 : 0;
   hipError_t e = mla_launch_combine(o_acc, lse_acc, num_splits, batch, R, (uint16_t*)out, lse, wide,
                                     stream);
+  return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+// Shapes of the absorption products: the decode's limits.
+static mla_status_t absorb_shape_ok(int32_t batch, int32_t s_q, int32_t h_q) {
+  if (batch <= 0 || s_q <= 0 || h_q <= 0) return MLA_ERR_INVALID_ARGUMENT;
+  if (batch > MLA_MAX_BATCH || !rows_ok(s_q, h_q)) return MLA_ERR_UNSUPPORTED;
+  return MLA_OK;
+}
+
+mla_status_t mla_absorb_query(const void* q_nope, const void* q_rope, const void* w_uk_t,
+                              int32_t batch, int32_t s_q, int32_t h_q, void* q_out,
+                              hipStream_t stream) {
+  if (!q_nope || !q_rope || !w_uk_t || !q_out) return MLA_ERR_INVALID_ARGUMENT;
+  if (((uintptr_t)q_nope | (uintptr_t)q_rope | (uintptr_t)w_uk_t | (uintptr_t)q_out) & 15)
+    return MLA_ERR_INVALID_ARGUMENT;
+  const mla_status_t st = absorb_shape_ok(batch, s_q, h_q);
+  if (st != MLA_OK) return st;
+  hipError_t e = mla_launch_absorb_query((const uint16_t*)q_nope, (const uint16_t*)q_rope,
+                                         (const uint16_t*)w_uk_t, batch * s_q, h_q,
+                                         (uint16_t*)q_out, stream);
+  return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+mla_status_t mla_absorb_output(const void* out, const void* w_uv, int32_t batch, int32_t s_q,
+                               int32_t h_q, void* o, hipStream_t stream) {
+  if (!out || !w_uv || !o) return MLA_ERR_INVALID_ARGUMENT;
+  if (((uintptr_t)out | (uintptr_t)w_uv | (uintptr_t)o) & 15) return MLA_ERR_INVALID_ARGUMENT;
+  const mla_status_t st = absorb_shape_ok(batch, s_q, h_q);
+  if (st != MLA_OK) return st;
+  hipError_t e = mla_launch_absorb_output((const uint16_t*)out, (const uint16_t*)w_uv,
+                                          batch * s_q, h_q, (uint16_t*)o, stream);
   return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 

@@ -16,6 +16,8 @@ from .mla_oracle import (  # noqa: F401
     softmax_weights,
     explicit_heads,
     absorb_query,
+    absorb_output,
+    absorb_ref,
     attend_chunks_and_merge,
     merge_partials,
 )

@@ -279,6 +279,34 @@ def absorb_query(q_c: np.ndarray, q_r: np.ndarray, W_UK: np.ndarray) -> np.ndarr
     return np.concatenate([np.einsum("hdk,hd->hk", W_UK, q_c), q_r], axis=1)
 
 
+def absorb_output(out: np.ndarray, W_UV: np.ndarray) -> np.ndarray:
+    """Per-head output ``W_UV[h] out[h]`` (512 -> 128 values): head h's values
+    are ``W_UV[h] c_t``, and the weights sum over tokens commutes with the
+    linear map (release note, MLA principles).  ``out [H,512]`` -> ``[H,128]``."""
+    return np.einsum("hdk,hk->hd", W_UV, out)
+
+
+def absorb_ref(case):
+    """Both absorption products of a ``workloads.AbsorbCase``, in float64 from
+    the exactly widened bf16 inputs: ``q_out [b,s_q,h,576]`` (from q_nope,
+    q_rope and w_uk as stored) and ``o [b,s_q,h,128]`` (from lat_out, w_uv).
+    Each query token is an independent application of ``absorb_query`` /
+    ``absorb_output``."""
+    qn = bf16_to_f64(case.q_nope)
+    qr = bf16_to_f64(case.q_rope)
+    wk = bf16_to_f64(case.w_uk)
+    wv = bf16_to_f64(case.w_uv)
+    lo = bf16_to_f64(case.lat_out)
+    b, s, h = case.batch, case.s_q, case.h_q
+    q_out = np.zeros((b, s, h, HEAD_DIM))
+    o = np.zeros((b, s, h, wv.shape[1]))
+    for bi in range(b):
+        for i in range(s):
+            q_out[bi, i] = absorb_query(qn[bi, i], qr[bi, i], wk)
+            o[bi, i] = absorb_output(lo[bi, i], wv)
+    return q_out, o
+
+
 # --------------------------------------------------------------------------
 # splitting the key range and merging by log-sum-exp
 # --------------------------------------------------------------------------

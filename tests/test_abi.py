@@ -104,6 +104,23 @@ def test_invalid_arguments_launch_nothing(lib):
     assert lib.mla_combine(one, 10, one, 4, 1, 16, 8, one, one, null) == 3
 
 
+def test_absorb_invalid_arguments_launch_nothing(lib):
+    null = ctypes.c_void_p(0)
+    one = ctypes.c_void_p(16)
+    i32 = ctypes.c_int32
+    # null, misaligned, non-positive and oversized shapes fail before any HIP call
+    assert lib.mla_absorb_query(null, one, one, 4, 1, 16, one, null) == 1
+    assert lib.mla_absorb_query(one, one, ctypes.c_void_p(24), 4, 1, 16, one, null) == 1
+    assert lib.mla_absorb_query(one, one, one, 0, 1, 16, one, null) == 1
+    assert lib.mla_absorb_query(one, one, one, 4, 1, 4096, one, null) == 2
+    assert lib.mla_absorb_query(one, one, one, 65537, 1, 2, one, null) == 2  # batch above the limit
+    assert lib.mla_absorb_output(one, null, 4, 1, 16, one, null) == 1
+    assert lib.mla_absorb_output(one, one, 4, -1, 16, one, null) == 1
+    assert lib.mla_absorb_output(ctypes.c_void_p(8), one, 4, 1, 16, one, null) == 1
+    assert lib.mla_absorb_output(one, one, 65537, 1, 16, one, null) == 2
+    del i32
+
+
 def test_product_path_does_not_import_the_oracle():
     pkg = os.path.join(ROOT, "mla_paged_kv_06_amd")
     for dirpath, _, files in os.walk(pkg):

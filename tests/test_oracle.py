@@ -14,6 +14,7 @@ import pytest
 
 import oracle
 from oracle import mla_oracle
+import workloads
 from workloads import make_case, make_config_case, CONFIGS, PAGE, HEAD_DIM, V_DIM
 from casebuild import case_from_values, permute_pool, read_golden
 
@@ -57,7 +58,7 @@ def test_absorbed_equals_explicit_heads():
     q_abs = oracle.absorb_query(q_c, q_r, W_UK)  # [H, 576]
     K = np.concatenate([c, r], axis=1)  # cache entries [c_t ; r_t]
     out, lse = oracle.attend_f64(q_abs, K, [T] * H, scale)
-    o_abs = np.einsum("hdk,hk->hd", W_UV, out)
+    o_abs = oracle.absorb_output(out, W_UV)
     assert np.allclose(lse, lse_exp, rtol=1e-12, atol=0)
     rel = np.linalg.norm(o_abs - o_exp) / np.linalg.norm(o_exp)
     assert rel < 1e-10
@@ -322,3 +323,57 @@ def test_planted_transposed_value_is_caught(monkeypatch):
     monkeypatch.setattr(mla_oracle, "attend_f64", bad)
     with pytest.raises(AssertionError):
         test_value_all_ones_gives_ones()
+
+
+# ---------------------------------------------------------------- absorption products
+def test_absorb_ref_bruteforce():
+    """Both absorption products against scalar fsum loops over every output
+    value of a tiny case (pins the index order of both einsums: a swapped
+    operand or axis changes values)."""
+    case = workloads.make_absorb_case(2, 2, 3, seed=41)
+    q_out, o = oracle.absorb_ref(case)
+    qn = oracle.bf16_to_f64(case.q_nope)
+    qr = oracle.bf16_to_f64(case.q_rope)
+    wk = oracle.bf16_to_f64(case.w_uk)
+    wv = oracle.bf16_to_f64(case.w_uv)
+    lo = oracle.bf16_to_f64(case.lat_out)
+    for b in range(2):
+        for i in range(2):
+            for h in range(3):
+                for c in range(0, 512, 37):
+                    ref = math.fsum(wk[h, d, c] * qn[b, i, h, d] for d in range(128))
+                    assert abs(q_out[b, i, h, c] - ref) <= 1e-12 * (1 + abs(ref))
+                assert np.array_equal(q_out[b, i, h, 512:], qr[b, i, h])
+                for d in range(0, 128, 11):
+                    ref = math.fsum(wv[h, d, c] * lo[b, i, h, c] for c in range(512))
+                    assert abs(o[b, i, h, d] - ref) <= 1e-12 * (1 + abs(ref))
+
+
+def test_absorb_layouts_of_the_inputs():
+    """The transposed query weight the HIP path reads holds the same values."""
+    case = workloads.make_absorb_case(1, 1, 2, seed=43)
+    assert case.w_uk_t.shape == (2, 512, 128)
+    assert np.array_equal(case.w_uk_t[1, 300, 7], case.w_uk[1, 7, 300])
+
+
+def test_absorbed_pipeline_equals_explicit_heads_per_token():
+    """absorb_ref's query and output products wrapped around the latent
+    attention give the explicit per-head attention for every query token."""
+    case = workloads.make_absorb_case(2, 1, 2, seed=47)
+    q_out, _ = oracle.absorb_ref(case)
+    rng = np.random.Generator(np.random.PCG64(53))
+    T = 29
+    c = rng.standard_normal((T, 512))
+    r = rng.standard_normal((T, 64))
+    K = np.concatenate([c, r], axis=1)
+    wk = oracle.bf16_to_f64(case.w_uk)
+    wv = oracle.bf16_to_f64(case.w_uv)
+    scale = 1.0 / math.sqrt(192.0)
+    for b in range(2):
+        qn = oracle.bf16_to_f64(case.q_nope[b, 0])
+        qr = oracle.bf16_to_f64(case.q_rope[b, 0])
+        o_exp, lse_exp = oracle.explicit_heads(c, r, qn, qr, wk, wv, scale)
+        out, lse = oracle.attend_f64(q_out[b, 0], K, [T] * 2, scale)
+        o_abs = oracle.absorb_output(out, wv)
+        assert np.allclose(lse, lse_exp, rtol=1e-12, atol=0)
+        assert np.linalg.norm(o_abs - o_exp) <= 1e-10 * np.linalg.norm(o_exp)

@@ -16,4 +16,8 @@ from .gen import (  # noqa: F401
     HEAD_DIM,
     V_DIM,
     PAGE,
+    AbsorbCase,
+    make_absorb_case,
+    NOPE_DIM,
+    ROPE_DIM,
 )

@@ -236,3 +236,46 @@ def make_config_case(k: int, poison_unused: bool = False, poison_tail: bool = Fa
         rng=rng,
         info=info,
     )
+
+
+# --------------------------------------------------------------------------
+# inputs of the absorption products around the decode
+# --------------------------------------------------------------------------
+NOPE_DIM = 128  # per-head query part before absorption, and value head width
+ROPE_DIM = 64
+
+
+@dataclass
+class AbsorbCase:
+    """Inputs of the query and output absorption for one batch of query
+    tokens, as raw bf16 bits.  ``w_uk`` and ``w_uv`` are the per-head
+    up-projections as stored, ``[h, 128, 512]`` (head h's key part is
+    ``w_uk[h] @ c``, its value ``w_uv[h] @ c`` for a 512-d latent c);
+    ``w_uk_t`` is ``w_uk`` with its last two axes swapped, the layout the
+    query absorption reads.  ``lat_out`` stands for a decode output."""
+    batch: int
+    s_q: int
+    h_q: int
+    seed: int
+    q_nope: np.ndarray   # uint16 [b, s_q, h, 128]
+    q_rope: np.ndarray   # uint16 [b, s_q, h, 64]
+    w_uk: np.ndarray     # uint16 [h, 128, 512]
+    w_uk_t: np.ndarray   # uint16 [h, 512, 128]
+    w_uv: np.ndarray     # uint16 [h, 128, 512]
+    lat_out: np.ndarray  # uint16 [b, s_q, h, 512]
+
+
+def make_absorb_case(batch: int, s_q: int, h_q: int, seed: int) -> AbsorbCase:
+    """Draw, in this order from PCG64(seed): q_nope and q_rope ~ N(0, 1), the
+    weights ~ N(0, 1/512) (so an absorbed query entry has variance 1/4 and an
+    output entry variance 1), and the latent output ~ N(0, 1)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    def draw(shape, sd=1.0):
+        return bf16_bits_from_f32(rng.standard_normal(shape, dtype=np.float32) * np.float32(sd))
+    q_nope = draw((batch, s_q, h_q, NOPE_DIM))
+    q_rope = draw((batch, s_q, h_q, ROPE_DIM))
+    w_uk = draw((h_q, NOPE_DIM, V_DIM), 1.0 / math.sqrt(V_DIM))
+    w_uv = draw((h_q, NOPE_DIM, V_DIM), 1.0 / math.sqrt(V_DIM))
+    lat_out = draw((batch, s_q, h_q, V_DIM))
+    w_uk_t = np.ascontiguousarray(w_uk.transpose(0, 2, 1))
+    return AbsorbCase(batch, s_q, h_q, seed, q_nope, q_rope, w_uk, w_uk_t, w_uv, lat_out)
