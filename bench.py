@@ -208,6 +208,77 @@ def absorption_rates(mla, b, s_q, h_q, seed, dev, launches_per_rep=None):
     return out
 
 
+def kv_append_rates(mla, seqlens, n_new, seed, dev, R=32):
+    """Time mla_kv_append appending n_new tokens to every sequence of this
+    workload (its lengths; a pool of exactly the held pages plus the free
+    ones).  Each of R launches in a graph works on its own copy of the
+    lengths and of the free count, reset before every replay outside the
+    timed region, so every launch does the same allocation and copies.  A
+    latency-bound step: a few hundred KB per launch."""
+    import torch
+
+    rng = np.random.Generator(np.random.PCG64(seed))
+    batch = len(seqlens)
+    held = [(int(L) + 63) // 64 for L in seqlens]
+    need = [(int(L) + n_new + 63) // 64 - h for L, h in zip(seqlens, held)]
+    max_pages = max(h + k for h, k in zip(held, need))
+    free = sum(need) + 8
+    num_pages = sum(held) + free
+    perm = rng.permutation(num_pages).astype(np.int32)
+    bt = np.full((batch, max_pages), -1, dtype=np.int32)
+    k = 0
+    for b, h in enumerate(held):
+        bt[b, :h] = perm[k:k + h]
+        k += h
+    kv = torch.empty((num_pages, 64, 576), dtype=torch.bfloat16, device=dev)
+    bt_d = torch.from_numpy(bt).to(dev)
+    fp = torch.from_numpy(perm[k:].copy()).to(dev)
+    new_kv = torch.randn((batch, n_new, 576), dtype=torch.float32, device=dev).to(torch.bfloat16)
+    sl0 = torch.tensor(np.asarray(seqlens, dtype=np.int32), device=dev)
+    sls = [sl0.clone() for _ in range(R)]
+    fcs = [torch.full((1,), free, dtype=torch.int32, device=dev) for _ in range(R)]
+    sts = [torch.empty((1,), dtype=torch.int32, device=dev) for _ in range(R)]
+
+    def reset():
+        for r in range(R):
+            sls[r].copy_(sl0)
+            fcs[r].fill_(free)
+        torch.cuda.synchronize()
+
+    def launches():
+        for r in range(R):
+            mla.kv_append(kv, bt_d, sls[r], new_kv, fp, fcs[r], sts[r])
+
+    reset()
+    launches()
+    torch.cuda.synchronize()
+    if any(int(st.cpu()[0]) != 0 for st in sts):
+        raise RuntimeError("kv_append reported a shortage in the timing setup")
+    reset()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        launches()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    times = []
+    for _ in range(5):
+        reset()
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1) / R)
+    ms = float(np.mean(times))
+    nb = 2 * batch * n_new * 576 * 2 + 8 * batch + 4 * sum(need) * 2
+    gbs = nb / (ms * 1e-3) / 1e9
+    return {"us": round(ms * 1e3, 3), "bytes": int(nb), "tokens": batch * n_new,
+            "new_pages": int(sum(need)), "GB_per_s": round(gbs, 2),
+            "hbm_frac": round(gbs / HBM_PEAK_GBS, 5), "launches_per_call": 2}
+
+
 def copy_calibration(mib, launches=5):
     """Plain device-to-device copies of a known size, for scaling the HBM byte
     counters (run under rocprofv3 --pmc)."""
@@ -425,7 +496,11 @@ def main():
         "mfma_frac": round(dec_tflops / BF16_PEAK_TFLOPS, 4),
     }
     if not args.no_next_rows:
-        res["next_rows"] = {"absorption": absorption_rates(mla, b, s_q, h_q, 2000 + k, dev)}
+        res["next_rows"] = {
+            "absorption": absorption_rates(mla, b, s_q, h_q, 2000 + k, dev),
+            "kv_append": kv_append_rates(mla, [int(x) for x in case.cache_seqlens], s_q, 3000 + k,
+                                         dev),
+        }
     if not args.no_cpu_baseline:
         print("# timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(case)

@@ -83,6 +83,7 @@ typedef enum {
 #define MLA_MAX_PARTS 4096   /* partitions of the key range (see below) */
 #define MLA_NOPE_DIM 128     /* per-head query part before absorption; value head width */
 #define MLA_ROPE_DIM 64      /* rotary part of the query and of the cache entry */
+#define MLA_MAX_APPEND 65536 /* new tokens per sequence in one mla_kv_append */
 
 /*
  * Number of key-range partitions used for `num_cus` compute units
@@ -187,6 +188,43 @@ mla_status_t mla_absorb_query(const void* q_nope, const void* q_rope, const void
  */
 mla_status_t mla_absorb_output(const void* out, const void* w_uv, int32_t batch, int32_t s_q,
                                int32_t h_q, void* o, hipStream_t stream);
+
+/*
+ * Paged KV append with page allocation, the step before each decode step.
+ * The cache is paged, 64 tokens per block (FlashMLA release note, paragraph
+ * on the released paged BF16 cache), and blocks are handed out on demand as
+ * sequences grow (Tom's Hardware FR article, paragraph on the techniques).
+ * Sequence b's n_new new cache entries (each [512 latent ; 64 rotary]) go to
+ * tokens L_b .. L_b + n_new - 1 of it: token t at page block_table[b][t/64],
+ * slot t % 64.  A sequence that crosses into pages it does not hold yet
+ * takes them from the free-page stack:
+ *   k_b = ceil((L_b + n_new)/64) - ceil(L_b/64) new pages; with
+ *   K_b = k_0 + .. + k_{b-1} and F = *free_count on entry, its i-th new page
+ *   is free_pages[F - 1 - (K_b + i)] and goes to block_table[b][ceil(L_b/64) + i];
+ *   on exit *free_count = F - (k_0 + .. + k_{batch-1}) and cache_seqlens[b] =
+ *   L_b + n_new.
+ * If the stack holds fewer pages than needed, or some ceil((L_b+n_new)/64)
+ * exceeds max_pages, nothing at all is written except *status = 1;
+ * otherwise *status = 0.
+ *   kv_cache      bf16 [num_pages][64][576], written
+ *   block_table   int32 [batch][max_pages]; the entries of held pages are read,
+ *                 the new ones written
+ *   cache_seqlens int32 [batch], read and advanced
+ *   new_kv        bf16 [batch][n_new][576] (may be null when n_new = 0)
+ *   free_pages    int32 [>= *free_count]: physical pages not in use (distinct,
+ *                 < num_pages; not checked)
+ *   free_count    int32 [1], status int32 [1]: device words
+ * Device pointers, kv_cache and new_kv 16-byte aligned, caller-owned;
+ * asynchronous on `stream` (two launches); allocates nothing.  Errors:
+ * MLA_ERR_INVALID_ARGUMENT (null or misaligned pointer, non-positive size,
+ * n_new < 0), MLA_ERR_UNSUPPORTED (batch > MLA_MAX_BATCH or n_new >
+ * MLA_MAX_APPEND), MLA_ERR_HIP.  Shortage of pages is reported through
+ * *status, on the device.
+ */
+mla_status_t mla_kv_append(void* kv_cache, int32_t num_pages, int32_t* block_table,
+                           int32_t max_pages, int32_t* cache_seqlens, int32_t batch,
+                           const void* new_kv, int32_t n_new, const int32_t* free_pages,
+                           int32_t* free_count, int32_t* status, hipStream_t stream);
 
 /* Static, human-readable text of a status code. */
 const char* mla_status_string(mla_status_t status);

@@ -33,6 +33,7 @@ __all__ = [
     "ROPE_DIM",
     "absorb_query",
     "absorb_output",
+    "kv_append",
 ]
 
 HEAD_DIM = 576
@@ -88,6 +89,8 @@ def load_library() -> ctypes.CDLL:
     lib.mla_absorb_query.restype = ctypes.c_int
     lib.mla_absorb_output.argtypes = [vp, vp, i32, i32, i32, vp, vp]
     lib.mla_absorb_output.restype = ctypes.c_int
+    lib.mla_kv_append.argtypes = [vp, i32, vp, i32, vp, i32, vp, i32, vp, vp, vp, vp]
+    lib.mla_kv_append.restype = ctypes.c_int
     lib.mla_status_string.argtypes = [ctypes.c_int]
     lib.mla_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -235,3 +238,31 @@ def absorb_output(out: torch.Tensor, w_uv: torch.Tensor, o: Optional[torch.Tenso
     _check("mla_absorb_output", load_library().mla_absorb_output(
         _ptr(out), _ptr(w_uv), batch, s_q, h_q, _ptr(o), _stream(stream)))
     return o
+
+
+def kv_append(kv_cache: torch.Tensor, block_table: torch.Tensor, cache_seqlens: torch.Tensor,
+              new_kv: torch.Tensor, free_pages: torch.Tensor, free_count: torch.Tensor,
+              status: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Append ``new_kv [b, n_new, 576]`` to each sequence's pages, taking new
+    pages from the top of the ``free_pages`` stack (``free_count [1]`` entries
+    valid); updates ``kv_cache``, ``block_table``, ``cache_seqlens`` and
+    ``free_count`` in place.  Returns the device status word (0 = done, 1 =
+    too few free pages or a table row too short: nothing written)."""
+    _need(kv_cache, "kv_cache", torch.bfloat16, 3)
+    _need(block_table, "block_table", torch.int32, 2)
+    _need(cache_seqlens, "cache_seqlens", torch.int32, 1)
+    _need(new_kv, "new_kv", torch.bfloat16, 3)
+    _need(free_pages, "free_pages", torch.int32, 1)
+    _need(free_count, "free_count", torch.int32, 1)
+    batch, n_new, d = new_kv.shape
+    if d != HEAD_DIM or kv_cache.shape[1] != PAGE_SIZE or kv_cache.shape[2] != HEAD_DIM:
+        raise ValueError("new_kv must be [b,n_new,576] and kv_cache [pages,64,576]")
+    if block_table.shape[0] != batch or cache_seqlens.shape[0] != batch:
+        raise ValueError("block_table / cache_seqlens batch mismatch")
+    if status is None:
+        status = torch.empty((1,), dtype=torch.int32, device=kv_cache.device)
+    _check("mla_kv_append", load_library().mla_kv_append(
+        _ptr(kv_cache), kv_cache.shape[0], _ptr(block_table), block_table.shape[1],
+        _ptr(cache_seqlens), batch, _ptr(new_kv), n_new, _ptr(free_pages), _ptr(free_count),
+        _ptr(status), _stream(stream)))
+    return status

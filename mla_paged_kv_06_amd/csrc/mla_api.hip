@@ -88,6 +88,12 @@ extern "C" hipError_t mla_launch_absorb_query(const uint16_t* q_c, const uint16_
 extern "C" hipError_t mla_launch_absorb_output(const uint16_t* lat_out, const uint16_t* w_uv,
                                                int M, int H, uint16_t* o, hipStream_t stream);
 
+extern "C" hipError_t mla_launch_kv_append(uint16_t* kv, int32_t* block_table, int max_pages,
+                                           int32_t* seqlens, int batch, const uint16_t* new_kv,
+                                           int n_new, const int32_t* free_pages,
+                                           int32_t* free_count, int32_t* status,
+                                           hipStream_t stream);
+
 extern "C" {
 
 int32_t mla_num_partitions(int32_t s_q, int32_t h_q, int32_t num_cus) {
@@ -214,6 +220,23 @@ mla_status_t mla_absorb_output(const void* out, const void* w_uv, int32_t batch,
   if (st != MLA_OK) return st;
   hipError_t e = mla_launch_absorb_output((const uint16_t*)out, (const uint16_t*)w_uv,
                                           batch * s_q, h_q, (uint16_t*)o, stream);
+  return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+mla_status_t mla_kv_append(void* kv_cache, int32_t num_pages, int32_t* block_table,
+                           int32_t max_pages, int32_t* cache_seqlens, int32_t batch,
+                           const void* new_kv, int32_t n_new, const int32_t* free_pages,
+                           int32_t* free_count, int32_t* status, hipStream_t stream) {
+  if (!kv_cache || !block_table || !cache_seqlens || !free_pages || !free_count || !status ||
+      (n_new > 0 && !new_kv))
+    return MLA_ERR_INVALID_ARGUMENT;
+  if (((uintptr_t)kv_cache | (uintptr_t)new_kv) & 15) return MLA_ERR_INVALID_ARGUMENT;
+  if (num_pages <= 0 || max_pages <= 0 || batch <= 0 || n_new < 0)
+    return MLA_ERR_INVALID_ARGUMENT;
+  if (batch > MLA_MAX_BATCH || n_new > MLA_MAX_APPEND) return MLA_ERR_UNSUPPORTED;
+  hipError_t e = mla_launch_kv_append((uint16_t*)kv_cache, block_table, max_pages, cache_seqlens,
+                                      batch, (const uint16_t*)new_kv, n_new, free_pages,
+                                      free_count, status, stream);
   return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 

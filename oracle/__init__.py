@@ -20,4 +20,5 @@ from .mla_oracle import (  # noqa: F401
     absorb_ref,
     attend_chunks_and_merge,
     merge_partials,
+    kv_append_ref,
 )

@@ -345,3 +345,44 @@ def attend_chunks_and_merge(Q: np.ndarray, K: np.ndarray, n_rows: Sequence[int],
         outs.append(o)
         lses.append(l)
     return merge_partials(outs, lses)
+
+
+# --------------------------------------------------------------------------
+# paged KV append with page allocation
+# --------------------------------------------------------------------------
+def kv_append_ref(kv_bits: np.ndarray, block_table: np.ndarray, seqlens: np.ndarray,
+                  new_kv_bits: np.ndarray, free_pages: np.ndarray, free_count: int):
+    """Append ``new_kv_bits [b, n, 576]`` to each sequence of a paged cache.
+
+    The cache is paged, 64 tokens per block, blocks handed out on demand as a
+    sequence grows (release note, released paged cache; Tom's Hardware FR
+    article, techniques paragraph).  Token ``t`` of sequence ``b`` lives at
+    page ``block_table[b, t // 64]``, slot ``t % 64``.  Sequence ``b`` needs
+    ``ceil((L+n)/64) - ceil(L/64)`` new pages; they are popped from the top
+    of the free-page stack (``free_pages[:free_count]``) in batch order, i.e.
+    sequence b's i-th new page is ``free_pages[F - 1 - (K_b + i)]``.  If the
+    stack is too short or a row of the table too short, nothing changes and
+    the status is 1.  Works on copies; returns
+    ``(kv, block_table, seqlens, free_count, status)``.
+    """
+    kv = kv_bits.copy()
+    bt = block_table.copy()
+    sl = seqlens.copy()
+    batch, n, _ = new_kv_bits.shape
+    max_pages = bt.shape[1]
+    old = [(int(L) + PAGE - 1) // PAGE for L in sl]
+    new = [(int(L) + n + PAGE - 1) // PAGE for L in sl]
+    need = [new[b] - old[b] for b in range(batch)]
+    if sum(need) > free_count or any(x > max_pages for x in new):
+        return kv, bt, sl, free_count, 1
+    taken = 0
+    for b in range(batch):
+        for i in range(need[b]):
+            bt[b, old[b] + i] = free_pages[free_count - 1 - taken]
+            taken += 1
+        L = int(sl[b])
+        for i in range(n):
+            t = L + i
+            kv[bt[b, t // PAGE], t % PAGE, :] = new_kv_bits[b, i, :]
+        sl[b] = L + n
+    return kv, bt, sl, free_count - taken, 0

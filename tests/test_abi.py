@@ -121,6 +121,23 @@ def test_absorb_invalid_arguments_launch_nothing(lib):
     del i32
 
 
+def test_kv_append_invalid_arguments_launch_nothing(lib):
+    null = ctypes.c_void_p(0)
+    one = ctypes.c_void_p(16)
+    args = [one, 10, one, 4, one, 3, one, 2, one, one, one, null]
+    assert lib.mla_kv_append(*args[:0], null, *args[1:]) == 1      # no cache
+    bad = list(args); bad[6] = ctypes.c_void_p(20)                 # misaligned new_kv
+    assert lib.mla_kv_append(*bad) == 1
+    bad = list(args); bad[7] = -1                                  # n_new < 0
+    assert lib.mla_kv_append(*bad) == 1
+    bad = list(args); bad[3] = 0                                   # max_pages
+    assert lib.mla_kv_append(*bad) == 1
+    bad = list(args); bad[10] = null                               # status word
+    assert lib.mla_kv_append(*bad) == 1
+    bad = list(args); bad[5] = 70000                               # batch above the limit
+    assert lib.mla_kv_append(*bad) == 2
+
+
 def test_product_path_does_not_import_the_oracle():
     pkg = os.path.join(ROOT, "mla_paged_kv_06_amd")
     for dirpath, _, files in os.walk(pkg):

@@ -377,3 +377,66 @@ def test_absorbed_pipeline_equals_explicit_heads_per_token():
         o_abs = oracle.absorb_output(out, wv)
         assert np.allclose(lse, lse_exp, rtol=1e-12, atol=0)
         assert np.linalg.norm(o_abs - o_exp) <= 1e-10 * np.linalg.norm(o_exp)
+
+
+# ---------------------------------------------------------------- paged KV append
+def _append_case(seqlens, n_new, free, seed, max_pages=None):
+    c = workloads.make_append_case(seqlens, n_new, free, seed, max_pages)
+    return c.kv, c.block_table, c.seqlens, c.new_kv, c.free_pages
+
+
+def test_kv_append_worked_example():
+    """Hand-worked allocation: lengths 63, 64, 0, 130 with 2 new tokens need
+    1, 1, 1, 0 new pages; the stack [10 11 12 13 14] (top = 14) gives 14, 13,
+    12 in batch order and keeps 2 entries."""
+    kv = np.zeros((15, PAGE, HEAD_DIM), dtype=np.uint16)
+    bt = np.full((4, 4), -1, dtype=np.int32)
+    bt[0, 0] = 0
+    bt[1, 0] = 1
+    bt[3, :3] = [2, 3, 4]
+    sl = np.array([63, 64, 0, 130], dtype=np.int32)
+    new_kv = np.arange(4 * 2 * HEAD_DIM, dtype=np.uint16).reshape(4, 2, HEAD_DIM)
+    free = np.array([10, 11, 12, 13, 14], dtype=np.int32)
+    kv2, bt2, sl2, fc, st = oracle.kv_append_ref(kv, bt, sl, new_kv, free, 5)
+    assert st == 0 and fc == 2
+    assert bt2[0, 1] == 14 and bt2[1, 1] == 13 and bt2[2, 0] == 12
+    assert list(sl2) == [65, 66, 2, 132]
+    # sequence 0: token 63 -> page 0 slot 63, token 64 -> page 14 slot 0
+    assert np.array_equal(kv2[0, 63], new_kv[0, 0]) and np.array_equal(kv2[14, 0], new_kv[0, 1])
+    # sequence 1: tokens 64, 65 -> page 13 slots 0, 1; sequence 3: page 4 slots 2, 3
+    assert np.array_equal(kv2[13, 1], new_kv[1, 1]) and np.array_equal(kv2[4, 3], new_kv[3, 1])
+    assert np.array_equal(kv2[12, 1], new_kv[2, 1])
+
+
+def test_kv_append_logical_view():
+    """After the append every sequence reads back as its old tokens followed
+    by the new ones, through its updated block table."""
+    seqlens = [0, 1, 63, 64, 65, 200, 127]
+    for n_new in (1, 2, 64, 130):
+        kv, bt, sl, new_kv, free = _append_case(seqlens, n_new, free=40, seed=n_new)
+        kv2, bt2, sl2, fc, st = oracle.kv_append_ref(kv, bt, sl, new_kv, free, len(free))
+        assert st == 0
+        for b, L in enumerate(seqlens):
+            before = oracle.gather_latents(kv, bt[b], L)
+            after = oracle.gather_latents(kv2, bt2[b], L + n_new)
+            assert np.array_equal(after[:L], before)
+            assert np.array_equal(after[L:], oracle.bf16_to_f64(new_kv[b]))
+        taken = [int(p) for b in range(len(seqlens)) for p in bt2[b] if p >= 0 and p not in bt[b]]
+        assert sorted(taken) == sorted(int(p) for p in free[fc:])  # the top of the stack
+        assert len(set(taken)) == len(taken)
+
+
+def test_kv_append_shortage_writes_nothing():
+    kv, bt, sl, new_kv, free = _append_case([63, 64, 0], 2, free=2, seed=9)
+    kv2, bt2, sl2, fc, st = oracle.kv_append_ref(kv, bt, sl, new_kv, free, len(free))
+    assert st == 1 and fc == 2
+    assert np.array_equal(kv2, kv) and np.array_equal(bt2, bt) and np.array_equal(sl2, sl)
+    # a table row too short also stops everything
+    kv, bt, sl, new_kv, free = _append_case([64], 1, free=4, seed=10, max_pages=1)
+    assert oracle.kv_append_ref(kv, bt, sl, new_kv, free, len(free))[4] == 1
+
+
+def test_kv_append_nothing_new():
+    kv, bt, sl, new_kv, free = _append_case([5, 64], 0, free=3, seed=11)
+    kv2, bt2, sl2, fc, st = oracle.kv_append_ref(kv, bt, sl, new_kv, free, len(free))
+    assert st == 0 and fc == 3 and np.array_equal(kv2, kv) and np.array_equal(sl2, sl)

@@ -20,4 +20,6 @@ from .gen import (  # noqa: F401
     make_absorb_case,
     NOPE_DIM,
     ROPE_DIM,
+    AppendCase,
+    make_append_case,
 )

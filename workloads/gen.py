@@ -279,3 +279,41 @@ def make_absorb_case(batch: int, s_q: int, h_q: int, seed: int) -> AbsorbCase:
     lat_out = draw((batch, s_q, h_q, V_DIM))
     w_uk_t = np.ascontiguousarray(w_uk.transpose(0, 2, 1))
     return AbsorbCase(batch, s_q, h_q, seed, q_nope, q_rope, w_uk, w_uk_t, w_uv, lat_out)
+
+
+# --------------------------------------------------------------------------
+# inputs of the paged KV append
+# --------------------------------------------------------------------------
+@dataclass
+class AppendCase:
+    """A paged cache, its block table and lengths, a stack of free pages and
+    the new cache entries to append, as raw bits.  Pool pages: the held ones,
+    then the free ones, then 3 spare pages that nothing references, all at
+    positions drawn by one permutation; unused table entries are -1."""
+    kv: np.ndarray          # uint16 [num_pages, 64, 576]
+    block_table: np.ndarray  # int32 [batch, max_pages]
+    seqlens: np.ndarray     # int32 [batch]
+    new_kv: np.ndarray      # uint16 [batch, n_new, 576]
+    free_pages: np.ndarray  # int32 [free]
+
+
+def make_append_case(seqlens: Sequence[int], n_new: int, free: int, seed: int,
+                     max_pages: Optional[int] = None) -> AppendCase:
+    """Draw, in this order from PCG64(seed): the pool permutation, the cache
+    pool ~ N(0, 1) and the new entries ~ N(0, 1), rounded to bf16."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    batch = len(seqlens)
+    held = [(int(L) + PAGE - 1) // PAGE for L in seqlens]
+    if max_pages is None:
+        max_pages = max(held + [1]) + (n_new + PAGE - 1) // PAGE + 1
+    num_pages = sum(held) + free + 3
+    perm = rng.permutation(num_pages).astype(np.int32)
+    kv = bf16_bits_from_f32(rng.standard_normal((num_pages, PAGE, HEAD_DIM), dtype=np.float32))
+    bt = np.full((batch, max_pages), -1, dtype=np.int32)
+    k = 0
+    for b, h in enumerate(held):
+        bt[b, :h] = perm[k:k + h]
+        k += h
+    free_pages = perm[k:k + free].copy()
+    new_kv = bf16_bits_from_f32(rng.standard_normal((batch, n_new, HEAD_DIM), dtype=np.float32))
+    return AppendCase(kv, bt, np.array(seqlens, dtype=np.int32), new_kv, free_pages)
