@@ -1,8 +1,12 @@
 #!/usr/bin/env python3
 """Benchmark of one paged MLA decode step on one MI355X.
 
-A step is the whole hot path over one batch: split-KV schedule
-(mla_get_metadata), decode (mla_decode_paged) and combine (mla_combine).
+A step is the whole hot path over one batch: split-KV schedule, decode
+(mla_decode_paged) and combine (mla_combine).  The schedule is a launch of
+its own (mla_get_metadata), except for workgroups of at most 16 query rows
+and at most 1024 sequences, where the decode computes the same partition
+itself at the start of the launch (tile_metadata NULL); --schedule separate
+forces the separate launch.
 Inputs are seeded synthetic workloads (workloads.CONFIGS), resident in HBM
 before timing starts; R replicas of the cache / queries / tables rotate so
 that consecutive steps never hit the 256 MB Infinity Cache with the same KV.
@@ -303,6 +307,8 @@ def main():
     ap.add_argument("--replicas", type=int, default=0, help="0 = enough to exceed 1 GiB")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--schedule", choices=["auto", "separate"], default="auto",
+                    help="auto: the decode schedules itself where it can")
     ap.add_argument("--no-next-rows", action="store_true",
                     help="skip timing the absorption products next to the decode")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -362,14 +368,21 @@ def main():
     def vp(t):
         return ctypes.c_void_p(t.data_ptr())
 
+    in_decode = args.schedule != "separate" and mla.schedules_in_decode(b, s_q, h_q)
+
+    def meta_arg(o):
+        return None if in_decode else vp(o["meta"])
+
     def step(r):
         q, kv, bt, sl = reps[r]
         o = bufs[r]
         st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
-        s1 = lib.mla_get_metadata(vp(sl), b, s_q, h_q, 0, vp(o["meta"]), vp(o["splits"]), st)
+        s1 = 0
+        if not in_decode:
+            s1 = lib.mla_get_metadata(vp(sl), b, s_q, h_q, 0, vp(o["meta"]), vp(o["splits"]), st)
         s2 = lib.mla_decode_paged(vp(q), vp(kv), vp(bt), vp(sl), b, s_q, h_q, case.num_pages,
                                   case.max_pages, case.softmax_scale, int(case.causal),
-                                  vp(o["meta"]), vp(o["splits"]), 0, vp(o["ws"]), ws_bytes,
+                                  meta_arg(o), vp(o["splits"]), 0, vp(o["ws"]), ws_bytes,
                                   vp(o["out"]), vp(o["lse"]), st)
         s3 = lib.mla_combine(vp(o["ws"]), ws_bytes, vp(o["splits"]), b, s_q, h_q, 0,
                              vp(o["out"]), vp(o["lse"]), st)
@@ -428,7 +441,7 @@ def main():
             st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
             st2 = lib.mla_decode_paged(vp(q), vp(kv), vp(bt), vp(sl), b, s_q, h_q, case.num_pages,
                                        case.max_pages, case.softmax_scale, int(case.causal),
-                                       vp(o["meta"]), vp(o["splits"]), 0, vp(o["ws"]), ws_bytes,
+                                       meta_arg(o), vp(o["splits"]), 0, vp(o["ws"]), ws_bytes,
                                        vp(o["out"]), vp(o["lse"]), st)
             if st2:
                 raise RuntimeError(f"decode status {st2}")
@@ -486,6 +499,7 @@ def main():
             "cache_seqlens": list(spec.lengths), "sum_seqlen": int(case.cache_seqlens.sum()),
             "causal": bool(case.causal), "seed": 1000 + k, "replicas": R,
             "timing": timing, "decode_launches_timed": n_rep * R,
+            "schedule": "in-decode" if in_decode else "separate-launch",
         },
         "algorithmic": {"bytes_per_step": int(nbytes), "flops_per_step": int(flops)},
         "tflops": round(flops / (ms_per_step * 1e-3) / 1e12, 3),

@@ -84,6 +84,7 @@ typedef enum {
 #define MLA_NOPE_DIM 128     /* per-head query part before absorption; value head width */
 #define MLA_ROPE_DIM 64      /* rotary part of the query and of the cache entry */
 #define MLA_MAX_APPEND 65536 /* new tokens per sequence in one mla_kv_append */
+#define MLA_MAX_FUSED_BATCH 1024 /* sequences for a decode that schedules itself */
 
 /*
  * Number of key-range partitions used for `num_cus` compute units
@@ -130,6 +131,12 @@ mla_status_t mla_get_metadata(const int32_t* cache_seqlens, int32_t batch, int32
  * written straight to out/lse; the others write float32 partials into the
  * workspace for mla_combine.  tile_metadata and num_splits must come from
  * mla_get_metadata with the same cache_seqlens, batch, s_q, h_q and num_cus.
+ * Alternatively, when s_q * h_q <= 16, batch <= MLA_MAX_FUSED_BATCH and
+ * batch * (max_pages + 2) < 2^30, tile_metadata may be NULL: the decode then
+ * computes the same schedule inside its launch (every workgroup for itself)
+ * and writes num_splits (batch + 1 ints, device) for mla_combine; other
+ * shapes with a NULL tile_metadata return MLA_ERR_UNSUPPORTED.  With
+ * tile_metadata given, num_splits is only read.
  * softmax_scale must be finite and positive (the pages' 1/sqrt(d) scaling);
  * anything else returns MLA_ERR_INVALID_ARGUMENT.
  */
@@ -137,7 +144,7 @@ mla_status_t mla_decode_paged(const void* q, const void* kv_cache, const int32_t
                               const int32_t* cache_seqlens, int32_t batch, int32_t s_q,
                               int32_t h_q, int32_t num_pages, int32_t max_pages,
                               float softmax_scale, int32_t causal, const int32_t* tile_metadata,
-                              const int32_t* num_splits, int32_t num_cus, void* workspace,
+                              int32_t* num_splits, int32_t num_cus, void* workspace,
                               size_t workspace_bytes, void* out, float* lse, hipStream_t stream);
 
 /*

@@ -34,12 +34,14 @@ __all__ = [
     "absorb_query",
     "absorb_output",
     "kv_append",
+    "schedules_in_decode",
 ]
 
 HEAD_DIM = 576
 V_DIM = 512
 PAGE_SIZE = 64
 META_INTS = 8
+MAX_FUSED_BATCH = 1024  # sequences for a decode that schedules itself
 NOPE_DIM = 128  # per-head query part before absorption; value head width
 ROPE_DIM = 64
 
@@ -155,10 +157,13 @@ def get_metadata(cache_seqlens: torch.Tensor, s_q: int, h_q: int, num_cus: int =
 
 def decode_paged(q: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Tensor,
                  cache_seqlens: torch.Tensor, softmax_scale: float, causal: bool,
-                 tile_metadata: torch.Tensor, num_splits: torch.Tensor, num_cus: int = 0,
-                 workspace: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
-                 lse: Optional[torch.Tensor] = None, stream=None):
-    """Decode (without the combine).  Returns ``(out, lse, workspace)``."""
+                 tile_metadata: Optional[torch.Tensor], num_splits: torch.Tensor,
+                 num_cus: int = 0, workspace: Optional[torch.Tensor] = None,
+                 out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                 stream=None):
+    """Decode (without the combine).  Returns ``(out, lse, workspace)``.  With
+    ``tile_metadata=None`` (at most 16 rows, at most 1024 sequences) the decode
+    schedules itself and writes ``num_splits``."""
     _need(q, "q", torch.bfloat16, 4)
     _need(kv_cache, "kv_cache", torch.bfloat16, 3)
     _need(block_table, "block_table", torch.int32, 2)
@@ -192,11 +197,27 @@ def combine(workspace: torch.Tensor, num_splits: torch.Tensor, batch: int, s_q: 
         s_q, h_q, num_cus, _ptr(out), _ptr(lse), _stream(stream)))
 
 
+def schedules_in_decode(batch: int, s_q: int, h_q: int) -> bool:
+    """Whether the decode can compute the split-KV schedule in its own launch."""
+    return s_q * h_q <= 16 and batch <= MAX_FUSED_BATCH
+
+
 def mla_decode(q, kv_cache, block_table, cache_seqlens, softmax_scale, causal, num_cus: int = 0,
-               stream=None):
-    """One full decode step: schedule, decode, combine.  Returns ``(out, lse)``."""
+               stream=None, schedule: str = "auto"):
+    """One full decode step: schedule, decode, combine.  Returns ``(out, lse)``.
+
+    ``schedule``: "separate" (mla_get_metadata, then the decode), "in_decode"
+    (the decode schedules itself; at most 16 rows and 1024 sequences) or
+    "auto" (in the decode when it can)."""
     batch, s_q, h_q, _ = q.shape
-    meta, splits = get_metadata(cache_seqlens, s_q, h_q, num_cus, stream)
+    if schedule not in ("auto", "separate", "in_decode"):
+        raise ValueError(f"unknown schedule {schedule!r}")
+    fused = schedule == "in_decode" or (schedule == "auto" and schedules_in_decode(batch, s_q, h_q))
+    if fused:
+        meta = None
+        splits = torch.empty((batch + 1,), dtype=torch.int32, device=q.device)
+    else:
+        meta, splits = get_metadata(cache_seqlens, s_q, h_q, num_cus, stream)
     out, lse, ws = decode_paged(q, kv_cache, block_table, cache_seqlens, softmax_scale, causal,
                                 meta, splits, num_cus, stream=stream)
     combine(ws, splits, batch, s_q, h_q, out, lse, num_cus, stream)

@@ -128,10 +128,10 @@ mla_status_t mla_decode_paged(const void* q, const void* kv_cache, const int32_t
                               const int32_t* cache_seqlens, int32_t batch, int32_t s_q,
                               int32_t h_q, int32_t num_pages, int32_t max_pages,
                               float softmax_scale, int32_t causal, const int32_t* tile_metadata,
-                              const int32_t* num_splits, int32_t num_cus, void* workspace,
+                              int32_t* num_splits, int32_t num_cus, void* workspace,
                               size_t workspace_bytes, void* out, float* lse, hipStream_t stream) {
-  if (!q || !kv_cache || !block_table || !cache_seqlens || !tile_metadata || !num_splits ||
-      !workspace || !out || !lse)
+  if (!q || !kv_cache || !block_table || !cache_seqlens || !num_splits || !workspace || !out ||
+      !lse)
     return MLA_ERR_INVALID_ARGUMENT;
   if (batch <= 0 || s_q <= 0 || h_q <= 0 || num_pages <= 0 || max_pages <= 0 || num_cus < 0)
     return MLA_ERR_INVALID_ARGUMENT;
@@ -143,6 +143,12 @@ mla_status_t mla_decode_paged(const void* q, const void* kv_cache, const int32_t
   if (parts <= 0) return MLA_ERR_HIP;
   const int R = s_q * h_q;
   if (workspace_bytes < ws_bytes(batch, R, parts)) return MLA_ERR_WORKSPACE_TOO_SMALL;
+  // without tile_metadata the decode schedules itself: workgroups of at most
+  // 16 rows, at most MLA_MAX_FUSED_BATCH sequences, and a block table small
+  // enough that its schedule units fit 32-bit arithmetic
+  if (!tile_metadata && (rows_variant_of(R) != 16 || batch > MLA_MAX_FUSED_BATCH ||
+                         (long long)batch * ((long long)max_pages + 2) >= (1LL << 30)))
+    return MLA_ERR_UNSUPPORTED;
 
   mla::DecodeParams prm;
   prm.q = (const uint16_t*)q;
@@ -164,6 +170,7 @@ mla_status_t mla_decode_paged(const void* q, const void* kv_cache, const int32_t
   prm.row_groups = row_groups_of(R);
   prm.causal = causal ? 1 : 0;
   prm.scale_log2 = (float)((double)softmax_scale * 1.4426950408889634);
+  prm.sched_c0 = fixed_cost_of(R);
   const int variant = rows_variant_of(R);
   hipError_t e = variant == 64   ? mla_launch_decode_sv64(&prm, stream)
                  : variant == 16 ? mla_launch_decode_t16(&prm, stream)

@@ -105,7 +105,7 @@ struct DecodeParams {
   const int32_t* block_table;
   const int32_t* seqlens;
   const int32_t* meta;
-  const int32_t* splits;
+  int32_t* splits;  // written by kernels that schedule in-launch
   uint16_t* out;
   float* lse;
   float* o_acc;    // [slots][R][512]
@@ -113,6 +113,7 @@ struct DecodeParams {
   int batch, s_q, h_q, R, max_pages, num_parts, row_groups;
   int causal;
   float scale_log2;  // softmax_scale * log2(e)
+  int sched_c0;      // fixed cost of the schedule rule (kernels that schedule in-launch)
 };
 
 }  // namespace mla

@@ -161,6 +161,57 @@ def test_forced_partition_counts(mla, num_cus):
     compare(out, lse, ref_out, ref_lse)
 
 
+def _both_schedules(mla, case, num_cus=0):
+    q, kv, bt, sl = to_dev(case)
+    res = {}
+    for sched in ("separate", "in_decode"):
+        meta, splits = None, None
+        if sched == "separate":
+            meta, splits = mla.get_metadata(sl, case.s_q, case.h_q, num_cus)
+        else:
+            splits = torch.full((case.batch + 1,), -7, dtype=torch.int32, device="cuda:0")
+        out, lse, ws = mla.decode_paged(q, kv, bt, sl, case.softmax_scale, case.causal, meta,
+                                        splits, num_cus)
+        mla.combine(ws, splits, case.batch, case.s_q, case.h_q, out, lse, num_cus)
+        torch.cuda.synchronize()
+        res[sched] = (out.view(torch.int16).cpu().numpy(), lse.cpu().numpy(), splits.cpu().numpy())
+    return res
+
+
+@pytest.mark.parametrize("L,s_q,h_q,num_cus", [
+    ([256], 1, 16, 0),
+    (EDGE_L, 1, 16, 0),
+    (EDGE_L, 2, 8, 3),
+    ([1, 200, 4097, 65, 0, 3000], 2, 8, 64),
+    ([0, 0, 0], 1, 1, 256),
+    ([5000] * 3, 1, 16, 1024),
+])
+def test_schedule_in_decode_matches_separate(mla, L, s_q, h_q, num_cus):
+    """The decode that schedules itself cuts the key range exactly as the
+    separate scheduler does: the same split counts and bit-identical output."""
+    _say(f"[parity] in-decode schedule L={L[:4]} s_q={s_q} h_q={h_q} num_cus={num_cus}")
+    case = make_case(L, s_q, h_q, s_q > 1, seed=71 + len(L), pool_factor=1.25,
+                     poison_unused=True, poison_tail=True)
+    r = _both_schedules(mla, case, num_cus)
+    assert np.array_equal(r["separate"][2], r["in_decode"][2]), "num_splits"
+    assert np.array_equal(r["separate"][0], r["in_decode"][0]), "out bits"
+    assert np.array_equal(r["separate"][1], r["in_decode"][1]), "lse"
+
+
+def test_schedule_in_decode_batch_limits(mla):
+    """1024 sequences schedule in the decode; 1025 need the separate one."""
+    _say("[parity] in-decode schedule at 1024 sequences")
+    rng = np.random.Generator(np.random.PCG64(73))
+    L = [int(x) for x in rng.integers(0, 200, size=1024)]
+    case = make_case(L, 1, 16, False, seed=74, pool_factor=1.1)
+    r = _both_schedules(mla, case)
+    assert np.array_equal(r["separate"][2], r["in_decode"][2])
+    assert np.array_equal(r["separate"][0], r["in_decode"][0])
+    q, kv, bt, sl = to_dev(make_case(L + [3], 1, 16, False, seed=75, pool_factor=1.1))
+    with pytest.raises(mla.MlaError):
+        mla.mla_decode(q, kv, bt, sl, 0.07, False, schedule="in_decode")
+
+
 def test_empty_and_single_token(mla):
     _say("[parity] empty / single-token sequences")
     case = make_case([0, 1, 0, 2], 1, 16, False, seed=29)
