@@ -212,6 +212,87 @@ def absorption_rates(mla, b, s_q, h_q, seed, dev, launches_per_rep=None):
     return out
 
 
+def query_token_rates(mla, seqlens, s_q, h_q, seed, dev):
+    """Time whole decode steps (schedule + decode + combine, the schedule
+    inside the decode where it can go) with s_q query tokens per sequence,
+    causal: several speculative tokens, or a chunk of new tokens at every
+    head.  The same kernels as the workloads above, more rows per sequence.
+    Replicas of cache, queries and tables (over 1 GiB in all) rotate in a
+    graph of back-to-back steps; HIP events around replays on the launch
+    stream."""
+    import ctypes
+
+    import torch
+    from workloads import make_case
+
+    case = make_case(seqlens, s_q, h_q, True, seed=seed, pool_factor=1.0)
+    nbytes, flops = algorithmic_work(case)
+    b = case.batch
+    lib = mla.load_library()
+    footprint = case.kv.nbytes + 2 * case.q.nbytes
+    R = max(2, math.ceil((1 << 30) / footprint))
+    up = lambda a: torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)  # noqa: E731
+    base = (up(case.q), up(case.kv), torch.from_numpy(case.block_table).to(dev),
+            torch.from_numpy(case.cache_seqlens).to(dev))
+    reps = [base] + [tuple(t.clone() for t in base) for _ in range(R - 1)]
+    parts = mla.num_partitions(s_q, h_q)
+    ws_bytes = mla.workspace_bytes(b, s_q, h_q)
+    in_decode = mla.schedules_in_decode(b, s_q, h_q)
+    bufs = [dict(meta=torch.empty((parts, mla.META_INTS), dtype=torch.int32, device=dev),
+                 splits=torch.empty((b + 1,), dtype=torch.int32, device=dev),
+                 ws=torch.empty((ws_bytes,), dtype=torch.uint8, device=dev),
+                 out=torch.empty((b, s_q, h_q, 512), dtype=torch.bfloat16, device=dev),
+                 lse=torch.empty((b, s_q, h_q), dtype=torch.float32, device=dev))
+            for _ in range(R)]
+    vp = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
+
+    def step(r):
+        q, kv, bt, sl = reps[r]
+        o = bufs[r]
+        st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        s1 = 0 if in_decode else lib.mla_get_metadata(vp(sl), b, s_q, h_q, 0, vp(o["meta"]),
+                                                      vp(o["splits"]), st)
+        s2 = lib.mla_decode_paged(vp(q), vp(kv), vp(bt), vp(sl), b, s_q, h_q, case.num_pages,
+                                  case.max_pages, case.softmax_scale, 1,
+                                  None if in_decode else vp(o["meta"]), vp(o["splits"]), 0,
+                                  vp(o["ws"]), ws_bytes, vp(o["out"]), vp(o["lse"]), st)
+        s3 = lib.mla_combine(vp(o["ws"]), ws_bytes, vp(o["splits"]), b, s_q, h_q, 0,
+                             vp(o["out"]), vp(o["lse"]), st)
+        if s1 or s2 or s3:
+            raise RuntimeError(f"library status {s1} {s2} {s3}")
+
+    for r in range(R):
+        step(r)
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        for r in range(R):
+            step(r)
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    times = []
+    for _ in range(5):
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1) / R)
+    ms = float(np.mean(times))
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    tf = flops / (ms * 1e-3) / 1e12
+    return {"batch": b, "s_q": s_q, "h_q": h_q, "rows_per_sequence": s_q * h_q, "causal": True,
+            "sum_seqlen": int(case.cache_seqlens.sum()), "partitions": parts,
+            "us_per_step": round(ms * 1e3, 2), "bytes": nbytes, "flops": flops,
+            "GB_per_s": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+            "TFLOP_per_s": round(tf, 2), "mfma_frac": round(tf / BF16_PEAK_TFLOPS, 4),
+            "replicas": R}
+
+
 def kv_append_rates(mla, seqlens, n_new, seed, dev, R=32):
     """Time mla_kv_append appending n_new tokens to every sequence of this
     workload (its lengths; a pool of exactly the held pages plus the free
@@ -514,6 +595,14 @@ def main():
             "absorption": absorption_rates(mla, b, s_q, h_q, 2000 + k, dev),
             "kv_append": kv_append_rates(mla, [int(x) for x in case.cache_seqlens], s_q, 3000 + k,
                                          dev),
+            # more query tokens per sequence: 4 speculative tokens on the
+            # memory-bound workload's sequences, and a 512-token chunk at
+            # 128 heads over a 4096-token cache
+            "query_tokens": {
+                "speculative_s_q4": query_token_rates(
+                    mla, [int(x) for x in make_config_case(2).cache_seqlens], 4, 16, 4002, dev),
+                "chunk_512x128": query_token_rates(mla, [4096], 512, 128, 4003, dev),
+            },
         }
     if not args.no_cpu_baseline:
         print("# timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)

@@ -79,7 +79,7 @@ typedef enum {
 #define MLA_PAGE_SIZE 64
 #define MLA_META_INTS 8      /* ints per partition in tile_metadata */
 #define MLA_MAX_BATCH 65536
-#define MLA_MAX_ROWS 2048    /* s_q * h_q */
+#define MLA_MAX_ROWS 65536   /* s_q * h_q, e.g. a 512-token chunk at 128 heads */
 #define MLA_MAX_PARTS 4096   /* partitions of the key range (see below) */
 #define MLA_NOPE_DIM 128     /* per-head query part before absorption; value head width */
 #define MLA_ROPE_DIM 64      /* rotary part of the query and of the cache entry */
@@ -100,7 +100,9 @@ size_t mla_metadata_ints(int32_t s_q, int32_t h_q, int32_t num_cus);
 /*
  * Bytes of workspace mla_decode_paged / mla_combine need: float32 partial
  * outputs and log-sum-exps for sequences whose keys are split over several
- * partitions, one slot per (sequence, split).
+ * partitions, one slot per (sequence, split).  With a single partition
+ * (s_q * h_q of 16384 rows or more on 256 CUs) nothing is split: 256 bytes,
+ * never written, and mla_combine launches nothing.
  */
 size_t mla_workspace_bytes(int32_t batch, int32_t s_q, int32_t h_q, int32_t num_cus);
 

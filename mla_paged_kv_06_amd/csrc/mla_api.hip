@@ -64,12 +64,17 @@ int parts_of(int32_t s_q, int32_t h_q, int32_t num_cus) {
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-// workspace: o_acc [slots][R][512] fp32, then lse_acc [slots][R] fp32
+// workspace: o_acc [slots][R][512] fp32, then lse_acc [slots][R] fp32.  With
+// one partition no sequence is split (it owns every unit), so no slot is
+// ever written; a token 256 bytes keep the pointer checks uniform.
+size_t slots_of(int batch, int parts) { return parts > 1 ? (size_t)batch + parts : 0; }
 size_t oacc_bytes(int batch, int R, int parts) {
-  return align_up((size_t)(batch + parts) * R * MLA_V_DIM * sizeof(float), 256);
+  return align_up(slots_of(batch, parts) * R * MLA_V_DIM * sizeof(float), 256);
 }
 size_t ws_bytes(int batch, int R, int parts) {
-  return oacc_bytes(batch, R, parts) + align_up((size_t)(batch + parts) * R * sizeof(float), 256);
+  const size_t n = oacc_bytes(batch, R, parts) +
+                   align_up(slots_of(batch, parts) * R * sizeof(float), 256);
+  return n > 256 ? n : 256;
 }
 
 }  // namespace
@@ -188,6 +193,7 @@ mla_status_t mla_combine(const void* workspace, size_t workspace_bytes, const in
   if (parts <= 0) return MLA_ERR_HIP;
   const int R = s_q * h_q;
   if (workspace_bytes < ws_bytes(batch, R, parts)) return MLA_ERR_WORKSPACE_TOO_SMALL;
+  if (parts == 1) return MLA_OK;  // one partition: nothing was split
   const float* o_acc = (const float*)workspace;
   const float* lse_acc = (const float*)((const char*)workspace + oacc_bytes(batch, R, parts));
   // many partitions per sequence on average: spread each row's partials over

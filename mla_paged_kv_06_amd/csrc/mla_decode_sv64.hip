@@ -114,12 +114,21 @@ __global__ void __launch_bounds__(sv::kThreadsSV, 1)
   const int g = lane >> 4;
 
   // XCD-aware mapping: the row groups of a partition share an XCD, so the
-  // pages they all read are fetched from HBM once into that XCD's L2
+  // pages they all read are fetched from HBM once into that XCD's L2.  With
+  // fewer than 8 partitions (thousands of rows) that would leave XCDs idle:
+  // consecutive workgroups then take consecutive row groups instead.
   const int bid = blockIdx.x;
-  const int xcd = bid & 7;
-  const int rr = bid >> 3;
-  const int rg = rr % prm.row_groups;
-  const int part = (rr / prm.row_groups) * 8 + xcd;
+  int rg, part;
+  if (prm.num_parts >= 8) {
+    const int rr = bid >> 3;
+    rg = rr % prm.row_groups;
+    part = (rr / prm.row_groups) * 8 + (bid & 7);
+  } else {
+    rg = bid % prm.row_groups;
+    part = bid / prm.row_groups;
+  }
+  rg = uni(rg);
+  part = uni(part);
   if (part >= prm.num_parts) return;
 
   const int32_t* m = meta + part * kMetaInts;
@@ -472,7 +481,8 @@ __global__ void __launch_bounds__(sv::kThreadsSV, 1)
 extern "C" hipError_t mla_launch_decode_sv64(const mla::DecodeParams* prm, hipStream_t stream) {
   using namespace mla;
   const int groups = (prm->num_parts + 7) / 8;
-  const dim3 grid(groups * 8 * prm->row_groups);
+  const dim3 grid(prm->num_parts >= 8 ? groups * 8 * prm->row_groups
+                                      : prm->num_parts * prm->row_groups);
   hipLaunchKernelGGL(decode_kernel_sv64, grid, dim3(sv::kThreadsSV), 0, stream, *prm, prm->q,
                      prm->kv, prm->block_table, prm->seqlens, prm->meta, prm->splits, prm->out,
                      prm->lse, prm->o_acc, prm->lse_acc);

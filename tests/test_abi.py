@@ -71,13 +71,21 @@ def test_partitions_and_sizes(lib):
     assert lib.mla_num_partitions(1, 16, 1) == 1
     assert lib.mla_num_partitions(2, 128, 3) == 1
     assert lib.mla_num_partitions(0, 16, 256) == 0
-    assert lib.mla_num_partitions(1, 4096, 256) == 0  # more rows than supported
+    # thousands of rows (query chunks): fewer partitions, down to one
+    assert lib.mla_num_partitions(3, 683, 256) == 7     # 2049 rows, 33 row groups
+    assert lib.mla_num_partitions(32, 128, 256) == 4    # 4096 rows
+    assert lib.mla_num_partitions(128, 128, 256) == 1   # 16384 rows
+    assert lib.mla_num_partitions(512, 128, 256) == 1   # 65536 rows, the limit
+    assert lib.mla_num_partitions(1, 65537, 256) == 0   # more rows than supported
     assert lib.mla_metadata_ints(1, 16, 256) == 256 * 8
     R = 16
     ws = lib.mla_workspace_bytes(8, 1, 16, 256)
     need = (8 + 256) * R * 512 * 4 + (8 + 256) * R * 4
     assert need <= ws <= need + 512
     assert lib.mla_workspace_bytes(0, 1, 16, 256) == 0
+    # one partition: nothing is ever split, a token workspace
+    assert lib.mla_workspace_bytes(4, 512, 128, 256) == 256
+    assert lib.mla_workspace_bytes(4, 2, 128, 1) == 256
 
 
 def test_invalid_arguments_launch_nothing(lib):
@@ -85,7 +93,7 @@ def test_invalid_arguments_launch_nothing(lib):
     one = ctypes.c_void_p(16)
     assert lib.mla_get_metadata(null, 4, 1, 16, 8, one, one, null) == 1
     assert lib.mla_get_metadata(one, 0, 1, 16, 8, one, one, null) == 1
-    assert lib.mla_get_metadata(one, 4, 1, 4096, 8, one, one, null) == 2
+    assert lib.mla_get_metadata(one, 4, 1, 65537, 8, one, one, null) == 2
     args = [one, one, one, one, 4, 1, 16, 10, 4, 0.1, 0, one, one, 8, one, 10 ** 9, one, one, null]
     bad = list(args); bad[0] = null
     assert lib.mla_decode_paged(*bad) == 1
@@ -119,7 +127,7 @@ def test_absorb_invalid_arguments_launch_nothing(lib):
     assert lib.mla_absorb_query(null, one, one, 4, 1, 16, one, null) == 1
     assert lib.mla_absorb_query(one, one, ctypes.c_void_p(24), 4, 1, 16, one, null) == 1
     assert lib.mla_absorb_query(one, one, one, 0, 1, 16, one, null) == 1
-    assert lib.mla_absorb_query(one, one, one, 4, 1, 4096, one, null) == 2
+    assert lib.mla_absorb_query(one, one, one, 4, 1, 65537, one, null) == 2
     assert lib.mla_absorb_query(one, one, one, 65537, 1, 2, one, null) == 2  # batch above the limit
     assert lib.mla_absorb_output(one, null, 4, 1, 16, one, null) == 1
     assert lib.mla_absorb_output(one, one, 4, -1, 16, one, null) == 1

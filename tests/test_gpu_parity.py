@@ -105,6 +105,47 @@ def test_config4_sampled_parity(mla):
     _say(f"[parity] workload 4 batches {pick}: {errs}")
 
 
+# ---------------------------------------------------------------- query chunks
+@pytest.mark.parametrize("L,s_q,h_q,causal,num_cus", [
+    ([500, 70], 3, 683, False, 0),            # 2049 rows: 33 row groups, 7 partitions
+    ([64, 1000, 2100], 32, 128, True, 0),     # 4096 rows: 4 partitions
+    ([200, 1500], 128, 128, True, 0),         # 16384 rows: one partition, no combine
+    ([300, 90, 1200], 16, 128, True, 5),      # 2048 rows on 5 CUs: one partition
+])
+def test_query_chunk_parity(mla, L, s_q, h_q, causal, num_cus):
+    """Thousands of query rows per sequence (a chunk of new tokens at every
+    head), the same decode: fewer partitions than XCDs, one partition (no
+    split, nothing to combine), full oracle."""
+    _say(f"[parity] chunk L={L} s_q={s_q} h_q={h_q} causal={causal} num_cus={num_cus}")
+    case = make_case(L, s_q, h_q, causal, seed=81 + s_q, pool_factor=1.25,
+                     poison_unused=True, poison_tail=True)
+    out, lse = run(mla, case, num_cus)
+    ref_out, ref_lse = oracle.decode_ref(case)
+    errs = compare(out, lse, ref_out, ref_lse)
+    _say(f"[parity] chunk: max|err| {errs[0]:.2e} norm {errs[1]:.2e} lse {errs[2]:.2e}")
+
+
+def test_query_chunk_at_the_row_limit(mla):
+    """65536 rows (512 query tokens x 128 heads, causal, 1024 row groups):
+    sampled rows against the oracle, one by one."""
+    _say("[parity] chunk of 512 tokens x 128 heads, sampled rows")
+    case = make_case([1024, 700], 512, 128, True, seed=83, pool_factor=1.25,
+                     poison_unused=True, poison_tail=True)
+    out, lse = run(mla, case)
+    rng = np.random.Generator(np.random.PCG64(84))
+    rows = [(0, 0, 0), (0, 511, 127), (1, 0, 5), (1, 511, 0), (0, 255, 64), (1, 300, 127)]
+    rows += [(int(b), int(i), int(h)) for b, i, h in zip(rng.integers(0, 2, 30),
+                                                          rng.integers(0, 512, 30),
+                                                          rng.integers(0, 128, 30))]
+    ref = oracle.decode_ref_rows(case, rows)
+    got_o = np.stack([out[b, i, h] for b, i, h in rows])
+    got_l = np.array([lse[b, i, h] for b, i, h in rows])
+    ref_o = np.stack([r[0] for r in ref])
+    ref_l = np.array([r[1] for r in ref])
+    errs = compare(got_o[None], got_l[None], ref_o[None], ref_l[None])
+    _say(f"[parity] chunk at the limit: {errs}")
+
+
 # ---------------------------------------------------------------- edge cases
 EDGE_L = [1, 63, 64, 65, 127, 128, 4097]
 
@@ -124,8 +165,8 @@ def test_edge_lengths(mla, h_q, s_q, causal):
                                              (3, 40, True), (4, 128, True), (16, 128, True)])
 def test_row_shapes(mla, s_q, h_q, causal):
     """Row counts R = s_q * h_q that are not multiples of 16 (partial row tiles
-    in every kernel variant), several row groups, and the largest supported R
-    (2048 rows: 32 row groups of 64)."""
+    in every kernel variant), several row groups, and 2048 rows (32 row
+    groups of 64, the most that still leaves 8 partitions on 256 CUs)."""
     _say(f"[parity] rows s_q={s_q} h_q={h_q} causal={causal}")
     case = make_case([1, 100, 700, 65, 0, 130], s_q, h_q, causal, seed=31 + s_q * h_q,
                      pool_factor=1.25, poison_unused=True, poison_tail=True)
