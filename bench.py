@@ -237,7 +237,7 @@ def query_token_rates(mla, seqlens, s_q, h_q, seed, dev):
     reps = [base] + [tuple(t.clone() for t in base) for _ in range(R - 1)]
     parts = mla.num_partitions(s_q, h_q)
     ws_bytes = mla.workspace_bytes(b, s_q, h_q)
-    in_decode = mla.schedules_in_decode(b, s_q, h_q)
+    in_decode = mla.prefers_in_decode(b, s_q, h_q, case.max_pages)
     bufs = [dict(meta=torch.empty((parts, mla.META_INTS), dtype=torch.int32, device=dev),
                  splits=torch.empty((b + 1,), dtype=torch.int32, device=dev),
                  ws=torch.empty((ws_bytes,), dtype=torch.uint8, device=dev),
@@ -388,8 +388,8 @@ def main():
     ap.add_argument("--replicas", type=int, default=0, help="0 = enough to exceed 1 GiB")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true")
-    ap.add_argument("--schedule", choices=["auto", "separate"], default="auto",
-                    help="auto: the decode schedules itself where it can")
+    ap.add_argument("--schedule", choices=["auto", "separate", "in_decode"], default="auto",
+                    help="auto: the decode schedules itself where that is faster")
     ap.add_argument("--no-next-rows", action="store_true",
                     help="skip timing the absorption products next to the decode")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -449,7 +449,8 @@ def main():
     def vp(t):
         return ctypes.c_void_p(t.data_ptr())
 
-    in_decode = args.schedule != "separate" and mla.schedules_in_decode(b, s_q, h_q)
+    in_decode = args.schedule == "in_decode" or (
+        args.schedule == "auto" and mla.prefers_in_decode(b, s_q, h_q, case.max_pages))
 
     def meta_arg(o):
         return None if in_decode else vp(o["meta"])

@@ -133,12 +133,12 @@ mla_status_t mla_get_metadata(const int32_t* cache_seqlens, int32_t batch, int32
  * written straight to out/lse; the others write float32 partials into the
  * workspace for mla_combine.  tile_metadata and num_splits must come from
  * mla_get_metadata with the same cache_seqlens, batch, s_q, h_q and num_cus.
- * Alternatively, when s_q * h_q <= 16, batch <= MLA_MAX_FUSED_BATCH and
+ * Alternatively, when batch <= MLA_MAX_FUSED_BATCH and
  * batch * (max_pages + 2) < 2^30, tile_metadata may be NULL: the decode then
  * computes the same schedule inside its launch (every workgroup for itself)
- * and writes num_splits (batch + 1 ints, device) for mla_combine; other
- * shapes with a NULL tile_metadata return MLA_ERR_UNSUPPORTED.  With
- * tile_metadata given, num_splits is only read.
+ * and writes num_splits (batch + 1 ints, device) for mla_combine; larger
+ * batches or block tables with a NULL tile_metadata return
+ * MLA_ERR_UNSUPPORTED.  With tile_metadata given, num_splits is only read.
  * softmax_scale must be finite and positive (the pages' 1/sqrt(d) scaling);
  * anything else returns MLA_ERR_INVALID_ARGUMENT.
  */

@@ -35,6 +35,7 @@ __all__ = [
     "absorb_output",
     "kv_append",
     "schedules_in_decode",
+    "prefers_in_decode",
 ]
 
 HEAD_DIM = 576
@@ -197,9 +198,19 @@ def combine(workspace: torch.Tensor, num_splits: torch.Tensor, batch: int, s_q: 
         s_q, h_q, num_cus, _ptr(out), _ptr(lse), _stream(stream)))
 
 
-def schedules_in_decode(batch: int, s_q: int, h_q: int) -> bool:
-    """Whether the decode can compute the split-KV schedule in its own launch."""
-    return s_q * h_q <= 16 and batch <= MAX_FUSED_BATCH
+def schedules_in_decode(batch: int, s_q: int, h_q: int, max_pages: int = 0) -> bool:
+    """Whether the decode can compute the split-KV schedule in its own launch
+    (at most 1024 sequences, and a block table small enough for its 32-bit
+    unit arithmetic)."""
+    return batch <= MAX_FUSED_BATCH and batch * (max_pages + 2) < (1 << 30)
+
+
+def prefers_in_decode(batch: int, s_q: int, h_q: int, max_pages: int = 0) -> bool:
+    """Whether the schedule inside the decode is the faster choice: measured
+    so for at most 16 rows per sequence (one schedule launch saved); with more
+    rows the launch it saves costs less than holding back every workgroup's
+    first copies until the schedule is done."""
+    return s_q * h_q <= 16 and schedules_in_decode(batch, s_q, h_q, max_pages)
 
 
 def mla_decode(q, kv_cache, block_table, cache_seqlens, softmax_scale, causal, num_cus: int = 0,
@@ -207,12 +218,13 @@ def mla_decode(q, kv_cache, block_table, cache_seqlens, softmax_scale, causal, n
     """One full decode step: schedule, decode, combine.  Returns ``(out, lse)``.
 
     ``schedule``: "separate" (mla_get_metadata, then the decode), "in_decode"
-    (the decode schedules itself; at most 16 rows and 1024 sequences) or
-    "auto" (in the decode when it can)."""
+    (the decode schedules itself; at most 1024 sequences) or "auto" (in the
+    decode when it can)."""
     batch, s_q, h_q, _ = q.shape
     if schedule not in ("auto", "separate", "in_decode"):
         raise ValueError(f"unknown schedule {schedule!r}")
-    fused = schedule == "in_decode" or (schedule == "auto" and schedules_in_decode(batch, s_q, h_q))
+    fused = schedule == "in_decode" or (
+        schedule == "auto" and prefers_in_decode(batch, s_q, h_q, int(block_table.shape[1])))
     if fused:
         meta = None
         splits = torch.empty((batch + 1,), dtype=torch.int32, device=q.device)

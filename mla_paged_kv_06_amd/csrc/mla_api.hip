@@ -148,10 +148,10 @@ mla_status_t mla_decode_paged(const void* q, const void* kv_cache, const int32_t
   if (parts <= 0) return MLA_ERR_HIP;
   const int R = s_q * h_q;
   if (workspace_bytes < ws_bytes(batch, R, parts)) return MLA_ERR_WORKSPACE_TOO_SMALL;
-  // without tile_metadata the decode schedules itself: workgroups of at most
-  // 16 rows, at most MLA_MAX_FUSED_BATCH sequences, and a block table small
-  // enough that its schedule units fit 32-bit arithmetic
-  if (!tile_metadata && (rows_variant_of(R) != 16 || batch > MLA_MAX_FUSED_BATCH ||
+  // without tile_metadata the decode schedules itself: at most
+  // MLA_MAX_FUSED_BATCH sequences, and a block table small enough that its
+  // schedule units fit 32-bit arithmetic
+  if (!tile_metadata && (batch > MLA_MAX_FUSED_BATCH ||
                          (long long)batch * ((long long)max_pages + 2) >= (1LL << 30)))
     return MLA_ERR_UNSUPPORTED;
 

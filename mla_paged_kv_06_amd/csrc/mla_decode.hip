@@ -39,6 +39,7 @@
 // access on gfx950 (about 85 B/clk per CU against 200 B/clk for ds_read_b128).
 
 #include "mla_decode_common.h"
+#include "mla_sched_inlaunch.h"
 
 namespace mla {
 
@@ -52,12 +53,13 @@ struct Variant {
   static constexpr int kKS = kD / 32;            // 18 k-steps of the score product
 };
 
-template <int RT, int RGW, int CGW>
+// kFused: no tile_metadata; every workgroup computes the schedule itself.
+template <int RT, int RGW, int CGW, bool kFused>
 __global__ void __launch_bounds__(kThreads, 1)
     decode_kernel(const DecodeParams prm, const uint16_t* __restrict__ q_ptr,
                   const uint16_t* __restrict__ kv_ptr, const int32_t* __restrict__ block_table,
                   const int32_t* __restrict__ seqlens, const int32_t* __restrict__ meta,
-                  const int32_t* __restrict__ splits, uint16_t* __restrict__ out_ptr,
+                  int32_t* __restrict__ splits, uint16_t* __restrict__ out_ptr,
                   float* __restrict__ lse_ptr, float* __restrict__ o_acc,
                   float* __restrict__ lse_acc) {
   using V = Variant<RT, RGW, CGW>;
@@ -66,6 +68,7 @@ __global__ void __launch_bounds__(kThreads, 1)
 
   __shared__ __attribute__((aligned(1024))) char tile0_[kTileBytes];
   __shared__ __attribute__((aligned(1024))) char tile1_[kTileBytes];
+  __shared__ std::conditional_t<kFused, InLaunchShared<kThreads>, char> sched_sh;
   MLA_LDS char* tile0 = (MLA_LDS char*)tile0_;
   MLA_LDS char* tile1 = (MLA_LDS char*)tile1_;
 
@@ -86,11 +89,29 @@ __global__ void __launch_bounds__(kThreads, 1)
   const int part = (rr / prm.row_groups) * 8 + xcd;
   if (part >= prm.num_parts) return;
 
-  const int32_t* m = meta + part * kMetaInts;
-  const int eb = uni(m[2]), ej = uni(m[3]);
-  Item cur = {uni(m[0]), uni(m[1])};
+  int eb, ej, split_idx;
+  Item cur;
+  int L0 = 0, phys0 = 0;  // in-launch schedule: the first item's length and page
+  if constexpr (kFused) {
+    // the separate scheduler's cuts, computed by this workgroup
+    const InLaunchStart st =
+        schedule_in_launch<kThreads>(sched_sh, part, prm.num_parts, prm.batch, prm.sched_c0,
+                                     prm.max_pages, seqlens, block_table, splits,
+                                     part == 0 && rg == 0);
+    cur = st.cur;
+    eb = st.eb;
+    ej = st.ej;
+    split_idx = st.split_idx;
+    L0 = st.L0;
+    phys0 = st.phys0;
+  } else {
+    const int32_t* m = meta + part * kMetaInts;
+    eb = uni(m[2]);
+    ej = uni(m[3]);
+    cur = Item{uni(m[0]), uni(m[1])};
+    split_idx = uni(m[4]);
+  }
   if (!item_before(cur, eb, ej)) return;
-  int split_idx = uni(m[4]);
 
   const int row_base = rg * V::kRows + wr * 16 * RT;  // first row of this wave
   const int col_base = wc * V::kColsPerWave;
@@ -129,10 +150,15 @@ __global__ void __launch_bounds__(kThreads, 1)
   PageLoader loader;
   loader.init(lane);
 
-  auto begin_segment = [&](int b) __attribute__((always_inline)) {
-    L = uni(seqlens[b]);
-    seg_s_lo = uni(splits[b]);
-    seg_nsplit = uni(splits[b + 1]) - seg_s_lo;
+  auto begin_segment = [&](int b, int Lb) __attribute__((always_inline)) {
+    L = Lb;
+    if constexpr (kFused) {
+      seg_s_lo = uni(split_of<kThreads>(sched_sh, b, prm.batch));
+      seg_nsplit = uni(split_of<kThreads>(sched_sh, b + 1, prm.batch)) - seg_s_lo;
+    } else {
+      seg_s_lo = uni(splits[b]);
+      seg_nsplit = uni(splits[b + 1]) - seg_s_lo;
+    }
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
       const int row = row_base + 16 * rt + l16;
@@ -381,14 +407,21 @@ __global__ void __launch_bounds__(kThreads, 1)
     }
     if (!has_next || nx.b != cur.b) {
       finish_segment(cur.b);
-      if (has_next) begin_segment(nx.b);
+      if (has_next) begin_segment(nx.b, uni(seqlens[nx.b]));
     }
     cur = nx;
     return has_next;
   };
 
-  begin_segment(cur.b);
-  load_item(tile0, cur);
+  if constexpr (kFused) {
+    // length and page of the first item were read with the schedule
+    begin_segment(cur.b, L0);
+    if (cur.j * kPage < L0)
+      loader.issue(tile0, kvbase + (size_t)phys0 * kTileBytes, L0 - cur.j * kPage, wave);
+  } else {
+    begin_segment(cur.b, uni(seqlens[cur.b]));
+    load_item(tile0, cur);
+  }
   while (true) {
     if (!step(tile0, tile1)) break;
     if (!step(tile1, tile0)) break;
@@ -408,16 +441,12 @@ extern "C" hipError_t mla_launch_decode(const mla::DecodeParams* prm, int rows_v
 #define MLA_DECODE_ARGS                                                                  \
   *prm, prm->q, prm->kv, prm->block_table, prm->seqlens, prm->meta, prm->splits, prm->out, \
       prm->lse, prm->o_acc, prm->lse_acc
-  switch (rows_variant) {
-    case 16:
-      hipLaunchKernelGGL((decode_kernel<1, 1, 4>), grid, block, 0, stream, MLA_DECODE_ARGS);
-      break;
-    case 32:
-      hipLaunchKernelGGL((decode_kernel<2, 1, 4>), grid, block, 0, stream, MLA_DECODE_ARGS);
-      break;
-    default:
-      return hipErrorInvalidValue;
-  }
+  // (16 rows run in mla_decode_t16.hip)
+  if (rows_variant != 32) return hipErrorInvalidValue;
+  if (prm->meta)
+    hipLaunchKernelGGL((decode_kernel<2, 1, 4, false>), grid, block, 0, stream, MLA_DECODE_ARGS);
+  else  // schedule inside the launch (batch <= kFusedMaxBatch, checked by the caller)
+    hipLaunchKernelGGL((decode_kernel<2, 1, 4, true>), grid, block, 0, stream, MLA_DECODE_ARGS);
 #undef MLA_DECODE_ARGS
   return hipGetLastError();
 }

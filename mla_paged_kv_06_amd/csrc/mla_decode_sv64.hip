@@ -38,6 +38,7 @@
 // own loop (the value waves' 128 accumulators, the score waves' query rows).
 
 #include "mla_decode_common.h"
+#include "mla_sched_inlaunch.h"
 
 #pragma clang diagnostic ignored "-Winline-asm"
 
@@ -93,12 +94,14 @@ struct SvSlot {
   bool valid;
 };
 
+// kFused: no tile_metadata; every workgroup computes the schedule itself.
+template <bool kFused>
 __global__ void __launch_bounds__(sv::kThreadsSV, 1)
     decode_kernel_sv64(const DecodeParams prm, const uint16_t* q_ptr,
                        const uint16_t* __restrict__ kv_ptr,
                        const int32_t* __restrict__ block_table,
                        const int32_t* __restrict__ seqlens, const int32_t* __restrict__ meta,
-                       const int32_t* __restrict__ splits, uint16_t* __restrict__ out_ptr,
+                       int32_t* __restrict__ splits, uint16_t* __restrict__ out_ptr,
                        float* __restrict__ lse_ptr, float* __restrict__ o_acc,
                        float* __restrict__ lse_acc) {
   using namespace sv;
@@ -106,6 +109,7 @@ __global__ void __launch_bounds__(sv::kThreadsSV, 1)
   __shared__ __attribute__((aligned(16))) bf16x8 pbuf[2][kRT][64];  // [step & 1][row tile][lane]
   __shared__ float alpha_buf[2][kRows];                            // [step & 1][row]
   __shared__ float stat_l[kRows];                                  // row sums at a segment end
+  __shared__ std::conditional_t<kFused, InLaunchShared<kThreadsSV>, char> sched_sh;
   MLA_LDS char* ring = (MLA_LDS char*)ring_;
 
   const int lane = threadIdx.x & 63;
@@ -131,11 +135,36 @@ __global__ void __launch_bounds__(sv::kThreadsSV, 1)
   part = uni(part);
   if (part >= prm.num_parts) return;
 
-  const int32_t* m = meta + part * kMetaInts;
-  const int eb = uni(m[2]), ej = uni(m[3]);
-  const int b0 = uni(m[0]), j0 = uni(m[1]);
+  int eb, ej, b0, j0, split0, L0 = 0, phys0 = 0;
+  if constexpr (kFused) {
+    // the separate scheduler's cuts, computed by this workgroup
+    const InLaunchStart st =
+        schedule_in_launch<kThreadsSV>(sched_sh, part, prm.num_parts, prm.batch, prm.sched_c0,
+                                       prm.max_pages, seqlens, block_table, splits,
+                                       part == 0 && rg == 0);
+    eb = st.eb;
+    ej = st.ej;
+    b0 = st.cur.b;
+    j0 = st.cur.j;
+    split0 = st.split_idx;
+    L0 = st.L0;
+    phys0 = st.phys0;
+  } else {
+    const int32_t* m = meta + part * kMetaInts;
+    eb = uni(m[2]);
+    ej = uni(m[3]);
+    b0 = uni(m[0]);
+    j0 = uni(m[1]);
+    split0 = uni(m[4]);
+  }
   if (!item_before(Item{b0, j0}, eb, ej)) return;
-  const int split0 = uni(m[4]);
+  // first split of sequence b (b = batch: slots used)
+  auto split_at = [&](int b) __attribute__((always_inline)) -> int {
+    if constexpr (kFused)
+      return uni(split_of<kThreadsSV>(sched_sh, b, prm.batch));
+    else
+      return uni(splits[b]);
+  };
   const int row0 = rg * kRows;
   const bool is_value = wave >= 4;
 
@@ -165,8 +194,13 @@ __global__ void __launch_bounds__(sv::kThreadsSV, 1)
   s0.b = b0;
   s0.j = j0;
   s0.h = 0;
-  s0.L = uni(seqlens[b0]);
-  s0.phys = is_value ? uni(block_table[(size_t)b0 * prm.max_pages + j0]) : 0;
+  if constexpr (kFused) {  // read with the schedule
+    s0.L = L0;
+    s0.phys = is_value ? phys0 : 0;
+  } else {
+    s0.L = uni(seqlens[b0]);
+    s0.phys = is_value ? uni(block_table[(size_t)b0 * prm.max_pages + j0]) : 0;
+  }
   s0.valid = true;
 
   if (!is_value) {
@@ -187,8 +221,8 @@ __global__ void __launch_bounds__(sv::kThreadsSV, 1)
     int seg_s_lo = 0, seg_nsplit = 0, split_idx = split0;
 
     auto begin_segment = [&](int b, int L) __attribute__((always_inline)) {
-      seg_s_lo = uni(splits[b]);
-      seg_nsplit = uni(splits[b + 1]) - seg_s_lo;
+      seg_s_lo = split_at(b);
+      seg_nsplit = split_at(b + 1) - seg_s_lo;
       const uint16_t* qrow = q_ptr + ((size_t)b * prm.R + (live ? qk_row : 0)) * kD + 8 * g;
       static_for<0, kKS>([&](auto kc) __attribute__((always_inline)) {
         qf[decltype(kc)::value] = *(const bf16x8*)(qrow + 32 * decltype(kc)::value);
@@ -324,8 +358,8 @@ __global__ void __launch_bounds__(sv::kThreadsSV, 1)
         o[decltype(rc)::value][decltype(cc)::value] = f32x4{0.f, 0.f, 0.f, 0.f};
       });
     });
-    int seg_s_lo = uni(splits[b0]);
-    int seg_nsplit = uni(splits[b0 + 1]) - seg_s_lo;
+    int seg_s_lo = split_at(b0);
+    int seg_nsplit = split_at(b0 + 1) - seg_s_lo;
     int split_idx = split0;
 
     // resource of a slot: its page's half h, bounded by the live tokens
@@ -458,8 +492,8 @@ __global__ void __launch_bounds__(sv::kThreadsSV, 1)
         if (seg_end) {
           finish_segment(sp.b);
           if (sc.valid) {
-            seg_s_lo = uni(splits[sc.b]);
-            seg_nsplit = uni(splits[sc.b + 1]) - seg_s_lo;
+            seg_s_lo = split_at(sc.b);
+            seg_nsplit = split_at(sc.b + 1) - seg_s_lo;
           }
         }
       } else if (s2.valid) {
@@ -483,8 +517,13 @@ extern "C" hipError_t mla_launch_decode_sv64(const mla::DecodeParams* prm, hipSt
   const int groups = (prm->num_parts + 7) / 8;
   const dim3 grid(prm->num_parts >= 8 ? groups * 8 * prm->row_groups
                                       : prm->num_parts * prm->row_groups);
-  hipLaunchKernelGGL(decode_kernel_sv64, grid, dim3(sv::kThreadsSV), 0, stream, *prm, prm->q,
-                     prm->kv, prm->block_table, prm->seqlens, prm->meta, prm->splits, prm->out,
-                     prm->lse, prm->o_acc, prm->lse_acc);
+  if (prm->meta)
+    hipLaunchKernelGGL(decode_kernel_sv64<false>, grid, dim3(sv::kThreadsSV), 0, stream, *prm,
+                       prm->q, prm->kv, prm->block_table, prm->seqlens, prm->meta, prm->splits,
+                       prm->out, prm->lse, prm->o_acc, prm->lse_acc);
+  else  // schedule inside the launch (batch <= kFusedMaxBatch, checked by the caller)
+    hipLaunchKernelGGL(decode_kernel_sv64<true>, grid, dim3(sv::kThreadsSV), 0, stream, *prm,
+                       prm->q, prm->kv, prm->block_table, prm->seqlens, prm->meta, prm->splits,
+                       prm->out, prm->lse, prm->o_acc, prm->lse_acc);
   return hipGetLastError();
 }

@@ -21,33 +21,14 @@
 // copies, then a barrier.
 
 #include "mla_decode_common.h"
+#include "mla_sched_inlaunch.h"
 
 namespace mla {
 
-// Most sequences a workgroup schedules for itself (its threads hold four
-// lengths each).
-constexpr int kFusedMaxBatch = 1024;
 
 namespace t16 {
 constexpr int kKS = kD / 32;  // 18 k-steps of the score product
 constexpr int kCT = 8;        // 16-column tiles per wave (128 columns)
-
-// Inclusive prefix sum over the 64 lanes of a wave, and the wave's total:
-// Hillis-Steele inside each row of 16 lanes by DPP row shifts (lanes shifted
-// in from outside the row add 0), then each row adds the totals of the rows
-// before it, read from lanes 15, 31 and 47.  VALU only.
-__device__ __forceinline__ int wave_incl_scan(int x, int lane, int* total) {
-  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, true);  // row_shr:1
-  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, true);  // row_shr:2
-  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, true);  // row_shr:4
-  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, true);  // row_shr:8
-  const int r0 = __builtin_amdgcn_readlane(x, 15), r1 = __builtin_amdgcn_readlane(x, 31);
-  const int r2 = __builtin_amdgcn_readlane(x, 47), r3 = __builtin_amdgcn_readlane(x, 63);
-  const int row = lane >> 4;
-  x += (row >= 1 ? r0 : 0) + (row >= 2 ? r1 : 0) + (row >= 3 ? r2 : 0);
-  *total = (r0 + r1) + (r2 + r3);
-  return x;
-}
 }  // namespace t16
 
 template <bool kFused>
@@ -64,8 +45,7 @@ __global__ void __launch_bounds__(kThreads, 1)
   __shared__ __attribute__((aligned(16))) bf16x8 pbuf[2][64];  // [32-token k-step][lane]
   __shared__ float mx_buf[kWaves][16];                          // [wave][row]: tile max
   __shared__ float stat_l[kWaves][16];                          // [wave][row]: weight sums
-  __shared__ int s_split[kFused ? kFusedMaxBatch : 1];  // in-launch split prefix, per wave
-  __shared__ int s_wt[kWaves];                           // ... and the waves' totals
+  __shared__ std::conditional_t<kFused, InLaunchShared<kThreads>, char> sched_sh;
   MLA_LDS char* tile0 = (MLA_LDS char*)tile0_;
   MLA_LDS char* tile1 = (MLA_LDS char*)tile1_;
 
@@ -82,15 +62,7 @@ __global__ void __launch_bounds__(kThreads, 1)
   int eb, ej, split_idx;
   Item cur;
   int L0 = 0, phys0 = 0;  // in-launch schedule: the first item's length and page
-  // first split of sequence b (b = batch: the total) of the in-launch schedule
-  // (every read is made, so they go out together)
-  auto split_of = [&](int b) __attribute__((always_inline)) -> int {
-    const int wv = b >> 8;  // the wave that scanned b
-    const int sv = s_split[min(b, kFusedMaxBatch - 1)];
-    const int a0 = s_wt[0], a1 = s_wt[1], a2 = s_wt[2], a3 = s_wt[3];
-    const int off = (wv >= 1 ? a0 : 0) + (wv >= 2 ? a1 : 0) + (wv >= 3 ? a2 : 0);
-    return b >= prm.batch ? (a0 + a1) + (a2 + a3) : sv + off;
-  };
+
   if constexpr (!kFused) {
     const int32_t* m = meta + part * kMetaInts;
     eb = uni(m[2]);
@@ -98,112 +70,16 @@ __global__ void __launch_bounds__(kThreads, 1)
     cur = Item{uni(m[0]), uni(m[1])};
     split_idx = uni(m[4]);
   } else {
-    // The split-KV schedule of the separate scheduler (same rule, same
-    // result), computed by every workgroup for itself: sequence b costs
-    // c0 + max(1, ceil(L_b / 64)) units, partition p starts at unit p * q,
-    // q = ceil(T / parts), and b is cut at every multiple of q inside its
-    // pages [A_b, A_b + n_b), A_b = U_b + c0.  32-bit arithmetic: the caller
-    // keeps batch * (max_pages + 2) below 2^30 and n_b is clamped to the
-    // block-table row, so no sum overflows.  Thread tid holds sequences
-    // 4 tid .. 4 tid + 3.  Two barriers: one for the unit total T, one
-    // before the results are read; the split prefix is kept per wave
-    // (s_split) plus the wave totals (s_wt), added up by its readers.
-    const int tid = threadIdx.x;
-    const int c0 = prm.sched_c0;
-    const int nb = prm.batch;
-    const int max_pages = prm.max_pages;
-    // every argument the prologue needs, in one round of scalar loads
-    asm volatile("" ::"s"(c0), "s"(nb), "s"(max_pages), "s"(seqlens), "s"(splits),
-                 "s"(block_table));
-    __shared__ int s_wu[kWaves];    // wave totals of the units
-    __shared__ int s_pos[2][5];     // where partitions part, part + 1 start:
-                                    // (sequence, page, split, length, physical page)
-    // four loads in flight at once: indexes past the batch read its last
-    // length and are dropped (a branch per load would serialise them)
-    int n4[4], c4 = 0, lv[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) lv[i] = seqlens[min(4 * tid + i, nb - 1)];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      int n = (lv[i] + kPage - 1) >> 6;
-      n = n < 1 ? 1 : (n > max_pages ? max_pages : n);
-      n = (4 * tid + i < nb) ? n : 0;
-      c4 += n > 0 ? c0 + n : 0;
-      n4[i] = n;
-    }
-    int wt;
-    int U = wave_incl_scan(c4, lane, &wt) - c4;  // exclusive, inside the wave
-    if (lane == 0) s_wu[wave] = wt;
-    __syncthreads();
-    const int w0 = s_wu[0], w1 = s_wu[1], w2 = s_wu[2], w3 = s_wu[3];
-    const int T = (w0 + w1) + (w2 + w3);
-    U += (wave >= 1 ? w0 : 0) + (wave >= 2 ? w1 : 0) + (wave >= 3 ? w2 : 0);
-    const unsigned q = ((unsigned)T + prm.num_parts - 1) / (unsigned)prm.num_parts;
-    const int u0 = part * (int)q;  // both below T + q < 2^31
-    const int u1 = u0 + (int)q;
-    int ns4[4], ns = 0;
-    // the sequence whose units [U_b, U_b + c0 + n_b) hold u0 (u1), if it is
-    // one of this thread's: (b, page, split, length) and (b, page)
-    int pb = -1, pj = 0, pf = 0, pL = 0, qb = -1, qj = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int b = 4 * tid + i;
-      const int A = U + c0;
-      const int fa = (int)((unsigned)A / q);
-      ns4[i] = (b < nb) ? 1 + (int)((unsigned)(A + n4[i] - 1) / q) - fa : 0;
-      ns += ns4[i];
-      const int Ue = A + n4[i];
-      const bool h0 = b < nb && U <= u0 && u0 < Ue;
-      const bool h1 = b < nb && U <= u1 && u1 < Ue;
-      pb = h0 ? b : pb;
-      pj = h0 ? (u0 > A ? u0 - A : 0) : pj;
-      pf = h0 ? (u0 > A ? part - fa : 0) : pf;
-      pL = h0 ? lv[i] : pL;
-      qb = h1 ? b : qb;
-      qj = h1 ? (u1 > A ? u1 - A : 0) : qj;
-      U += (b < nb) ? c0 + n4[i] : 0;
-    }
-    // the first page's block-table entry, read while the split counts are
-    // scanned (threads without it read entry 0 and drop it)
-    const bool p_live = pb >= 0 && pj * kPage < pL;
-    const int ph = block_table[p_live ? (size_t)pb * max_pages + pj : 0];
-    int S = wave_incl_scan(ns, lane, &wt) - ns;  // exclusive, inside the wave
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int b = 4 * tid + i;
-      if (b < nb) s_split[b] = S;
-      S += ns4[i];
-    }
-    if (lane == 0) s_wt[wave] = wt;
-    if (pb >= 0) {
-      s_pos[0][0] = pb;
-      s_pos[0][1] = pj;
-      s_pos[0][2] = pf;
-      s_pos[0][3] = pL;
-      s_pos[0][4] = p_live ? ph : 0;
-    }
-    if (qb >= 0) {
-      s_pos[1][0] = qb;
-      s_pos[1][1] = qj;
-    }
-    if (tid == 0) {
-      // a start at or past the last unit is the end of the batch
-      if (u0 >= T) s_pos[0][0] = nb, s_pos[0][1] = 0, s_pos[0][2] = 0, s_pos[0][3] = 0;
-      if (u1 >= T) s_pos[1][0] = nb, s_pos[1][1] = 0;
-    }
-    __syncthreads();
-    if (part == 0) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (4 * tid + i < nb) splits[4 * tid + i] = split_of(4 * tid + i);
-      if (tid == 0) splits[nb] = split_of(nb);
-    }
-    cur = Item{uni(s_pos[0][0]), uni(s_pos[0][1])};
-    eb = uni(s_pos[1][0]);
-    ej = uni(s_pos[1][1]);
-    split_idx = uni(s_pos[0][2]);
-    L0 = uni(s_pos[0][3]);
-    phys0 = uni(s_pos[0][4]);
+    // the separate scheduler's cuts, computed by this workgroup
+    const InLaunchStart st = schedule_in_launch<kThreads>(
+        sched_sh, part, prm.num_parts, prm.batch, prm.sched_c0, prm.max_pages, seqlens,
+        block_table, splits, part == 0);
+    cur = st.cur;
+    eb = st.eb;
+    ej = st.ej;
+    split_idx = st.split_idx;
+    L0 = st.L0;
+    phys0 = st.phys0;
   }
   if (!item_before(cur, eb, ej)) return;
 
@@ -239,8 +115,8 @@ __global__ void __launch_bounds__(kThreads, 1)
   auto begin_segment = [&](int b, int Lb) __attribute__((always_inline)) {
     L = Lb;
     if constexpr (kFused) {
-      seg_s_lo = uni(split_of(b));
-      seg_nsplit = uni(split_of(b + 1)) - seg_s_lo;
+      seg_s_lo = uni(split_of<kThreads>(sched_sh, b, prm.batch));
+      seg_nsplit = uni(split_of<kThreads>(sched_sh, b + 1, prm.batch)) - seg_s_lo;
     } else {
       seg_s_lo = uni(splits[b]);
       seg_nsplit = uni(splits[b + 1]) - seg_s_lo;

@@ -108,10 +108,10 @@ def test_invalid_arguments_launch_nothing(lib):
     assert lib.mla_decode_paged(*bad) == 3
     bad = list(args); bad[0] = ctypes.c_void_p(18)  # misaligned q
     assert lib.mla_decode_paged(*bad) == 1
-    # no tile_metadata: only workgroups of at most 16 rows and 1024 sequences
-    bad = list(args); bad[11] = null; bad[6] = 32                 # h_q = 32
-    assert lib.mla_decode_paged(*bad) == 2
+    # no tile_metadata: at most 1024 sequences, batch * (max_pages + 2) < 2^30
     bad = list(args); bad[11] = null; bad[4] = 2000               # batch above 1024
+    assert lib.mla_decode_paged(*bad) == 2
+    bad = list(args); bad[11] = null; bad[4] = 1024; bad[8] = 1 << 20   # 1024 * (2^20 + 2) >= 2^30
     assert lib.mla_decode_paged(*bad) == 2
     bad = list(args); bad[12] = null                               # num_splits is always needed
     assert lib.mla_decode_paged(*bad) == 1

@@ -226,6 +226,12 @@ def _both_schedules(mla, case, num_cus=0):
     ([1, 200, 4097, 65, 0, 3000], 2, 8, 64),
     ([0, 0, 0], 1, 1, 256),
     ([5000] * 3, 1, 16, 1024),
+    (EDGE_L, 2, 16, 0),                        # 32 rows: the 4-wave 32-row kernel
+    (EDGE_L, 1, 64, 0),                        # 64 rows: the 64-row kernel
+    ([1, 200, 4097, 65, 0, 3000], 1, 64, 7),   # 64 rows, 7 partitions
+    ([700, 0, 2100, 64], 2, 128, 0),           # 4 row groups x 64 partitions
+    ([300, 1200], 32, 128, 0),                 # 64 row groups, 4 partitions
+    ([900, 65], 3, 40, 1),                     # 120 rows, one partition
 ])
 def test_schedule_in_decode_matches_separate(mla, L, s_q, h_q, num_cus):
     """The decode that schedules itself cuts the key range exactly as the
