@@ -111,12 +111,23 @@ def cpu_baseline(case, budget_s=20.0, min_s=10.0):
     }
 
 
-KERNEL_SOURCES = ("mla_paged_kv_06_amd/csrc", "include", "mla_paged_kv_06_amd/build.py")
+# what the decode kernels are built from (the HBM counters belong to them)
+KERNEL_SOURCES = (
+    "mla_paged_kv_06_amd/csrc/mla_decode_t16.hip",
+    "mla_paged_kv_06_amd/csrc/mla_decode.hip",
+    "mla_paged_kv_06_amd/csrc/mla_decode_sv64.hip",
+    "mla_paged_kv_06_amd/csrc/mla_decode_common.h",
+    "mla_paged_kv_06_amd/csrc/mla_sched_inlaunch.h",
+    "mla_paged_kv_06_amd/csrc/mla_device.h",
+    "mla_paged_kv_06_amd/csrc/mla_api.hip",
+    "include",
+    "mla_paged_kv_06_amd/build.py",
+)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
 def kernel_source_hash():
-    """sha256 over the HIP sources, headers and build flags of the library."""
+    """sha256 over the sources, headers and build flags of the decode kernels."""
     import hashlib
 
     h = hashlib.sha256()
