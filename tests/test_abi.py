@@ -160,3 +160,18 @@ def test_product_path_does_not_import_the_oracle():
             if f.endswith((".py", ".hip", ".h", ".cpp")):
                 text = open(os.path.join(dirpath, f)).read()
                 assert "oracle" not in text.replace("oracle_", ""), f
+
+
+def test_schedule_policy_of_the_binding():
+    """Which decodes schedule themselves: capability (at most 1024 sequences,
+    a block table within the 32-bit unit range) and the faster-path choice
+    (at most 16 rows); pure host logic."""
+    pytest.importorskip("torch")
+    import mla_paged_kv_06_amd as m
+
+    assert m.schedules_in_decode(1024, 1, 128, 64)
+    assert not m.schedules_in_decode(1025, 1, 16, 64)
+    assert not m.schedules_in_decode(1024, 1, 16, 1 << 20)   # 1024 * (2^20 + 2) >= 2^30
+    assert m.prefers_in_decode(8, 1, 16, 64)
+    assert not m.prefers_in_decode(8, 2, 16, 64)              # 32 rows: separate launch
+    assert not m.prefers_in_decode(2000, 1, 16, 64)
