@@ -105,6 +105,29 @@ def test_config4_sampled_parity(mla):
     _say(f"[parity] workload 4 batches {pick}: {errs}")
 
 
+def test_batch_at_the_limit(mla):
+    """65536 sequences (the batch limit), one query row each: one in 64 holds
+    1 to 200 tokens, the rest are empty.  The chunked scheduler's largest
+    case; the empty rows must come out as 0 / -inf, sampled live ones
+    against the oracle."""
+    _say("[parity] 65536 sequences")
+    batch = 65536
+    rng = np.random.Generator(np.random.PCG64(91))
+    L = np.zeros(batch, dtype=np.int64)
+    live = np.arange(0, batch, 64) + rng.integers(0, 64, batch // 64)
+    L[live] = rng.integers(1, 201, live.size)
+    case = make_case([int(x) for x in L], 1, 1, False, seed=92, pool_factor=1.1,
+                     poison_unused=True, poison_tail=True)
+    out, lse = run(mla, case)
+    empty = L == 0
+    assert np.all(np.isneginf(lse[empty])) and np.all(out[empty] == 0.0)
+    assert np.all(np.isfinite(lse[~empty]))
+    pick = sorted(set([int(live[0]), int(live[-1])] + [int(x) for x in rng.choice(live, 30)]))
+    ref_out, ref_lse = oracle.decode_ref(case, batches=pick)
+    errs = compare(out, lse, ref_out, ref_lse, batches=pick)
+    _say(f"[parity] 65536 sequences, {len(pick)} sampled: {errs}")
+
+
 # ---------------------------------------------------------------- query chunks
 @pytest.mark.parametrize("L,s_q,h_q,causal,num_cus", [
     ([500, 70], 3, 683, False, 0),            # 2049 rows: 33 row groups, 7 partitions
@@ -192,7 +215,7 @@ def test_many_short_sequences(mla, h_q):
     compare(out, lse, ref_out, ref_lse, batches=pick)
 
 
-@pytest.mark.parametrize("num_cus", [1, 3, 64, 256, 1024])
+@pytest.mark.parametrize("num_cus", [1, 3, 64, 256, 1024, 4096, 5000])
 def test_forced_partition_counts(mla, num_cus):
     _say(f"[parity] num_cus={num_cus}")
     case = make_case([1, 200, 4097, 65, 0, 3000], 2, 16, True, seed=23, pool_factor=1.25,
