@@ -22,3 +22,4 @@ from .mla_oracle import (  # noqa: F401
     merge_partials,
     kv_append_ref,
 )
+from . import fp8_cache  # noqa: F401  (FP8 latent cache: format, quantize, dequantize)
