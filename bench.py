@@ -304,6 +304,88 @@ def query_token_rates(mla, seqlens, s_q, h_q, seed, dev):
             "replicas": R}
 
 
+def fp8_cache_rates(mla, case, dev):
+    """Time the decode step over the FP8 latent cache (schedule + FP8 decode
+    + combine) on this workload's sequences and queries, the cache quantized
+    on the GPU beforehand; replicas of cache, queries and tables (over 1 GiB)
+    rotate in a graph of back-to-back steps, HIP events on the launch stream.
+    Algorithmic bytes count 656 per cached token instead of 1152."""
+    import ctypes
+
+    import torch
+
+    b, s_q, h_q = case.batch, case.s_q, case.h_q
+    if s_q * h_q > 16:
+        return {"skipped": "the FP8-cache decode takes at most 16 query rows per sequence"}
+    lib = mla.load_library()
+    L = case.cache_seqlens.astype(np.int64)
+    R_ = s_q * h_q
+    nbytes = int(656 * L.sum() + 1152 * b * R_ + 1024 * b * R_ + 4 * b * R_ +
+                 4 * ((L + 63) // 64).sum() + 4 * b)
+    q0 = torch.from_numpy(case.q.view(np.int16)).to(dev).view(torch.bfloat16)
+    kv0 = mla.kv_quantize_fp8(torch.from_numpy(case.kv.view(np.int16)).to(dev).view(torch.bfloat16))
+    bt0 = torch.from_numpy(case.block_table).to(dev)
+    sl0 = torch.from_numpy(case.cache_seqlens).to(dev)
+    R = max(2, math.ceil((1 << 30) / (kv0.numel() + 2 * q0.numel())))
+    reps = [(q0, kv0, bt0, sl0)] + [(q0.clone(), kv0.clone(), bt0.clone(), sl0.clone())
+                                   for _ in range(R - 1)]
+    parts = mla.num_partitions(s_q, h_q)
+    ws_bytes = mla.workspace_bytes(b, s_q, h_q)
+    bufs = [dict(meta=torch.empty((parts, mla.META_INTS), dtype=torch.int32, device=dev),
+                 splits=torch.empty((b + 1,), dtype=torch.int32, device=dev),
+                 ws=torch.empty((ws_bytes,), dtype=torch.uint8, device=dev),
+                 out=torch.empty((b, s_q, h_q, 512), dtype=torch.bfloat16, device=dev),
+                 lse=torch.empty((b, s_q, h_q), dtype=torch.float32, device=dev))
+            for _ in range(R)]
+    vp = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
+
+    def step(r, full=True):
+        q, kv, bt, sl = reps[r]
+        o = bufs[r]
+        st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        s1 = lib.mla_get_metadata(vp(sl), b, s_q, h_q, 0, vp(o["meta"]), vp(o["splits"]), st) \
+            if full else 0
+        s2 = lib.mla_decode_paged_fp8(vp(q), vp(kv), vp(bt), vp(sl), b, s_q, h_q,
+                                      kv.shape[0], case.max_pages, case.softmax_scale,
+                                      int(case.causal), vp(o["meta"]), vp(o["splits"]), 0,
+                                      vp(o["ws"]), ws_bytes, vp(o["out"]), vp(o["lse"]), st)
+        s3 = lib.mla_combine(vp(o["ws"]), ws_bytes, vp(o["splits"]), b, s_q, h_q, 0,
+                             vp(o["out"]), vp(o["lse"]), st) if full else 0
+        if s1 or s2 or s3:
+            raise RuntimeError(f"library status {s1} {s2} {s3}")
+
+    res = {}
+    for name, full in (("step", True), ("decode", False)):
+        for r in range(R):
+            step(r, True)
+        torch.cuda.synchronize()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            for r in range(R):
+                step(r, full)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        times = []
+        for _ in range(5):
+            e0.record()
+            g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1) / R)
+        res[name] = float(np.mean(times))
+    gbs = nbytes / (res["step"] * 1e-3) / 1e9
+    dgbs = nbytes / (res["decode"] * 1e-3) / 1e9
+    return {"us_per_step": round(res["step"] * 1e3, 2), "decode_us": round(res["decode"] * 1e3, 2),
+            "bytes": nbytes, "GB_per_s": round(gbs, 1), "decode_GB_per_s": round(dgbs, 1),
+            "decode_hbm_frac": round(dgbs / HBM_PEAK_GBS, 4), "token_bytes": 656,
+            "replicas": R}
+
+
 def kv_append_rates(mla, seqlens, n_new, seed, dev, R=32):
     """Time mla_kv_append appending n_new tokens to every sequence of this
     workload (its lengths; a pool of exactly the held pages plus the free
@@ -610,6 +692,7 @@ def main():
             # more query tokens per sequence: 4 speculative tokens on the
             # memory-bound workload's sequences, and a 512-token chunk at
             # 128 heads over a 4096-token cache
+            "fp8_cache": fp8_cache_rates(mla, case, dev),
             "query_tokens": {
                 "speculative_s_q4": query_token_rates(
                     mla, [int(x) for x in make_config_case(2).cache_seqlens], 4, 16, 4002, dev),

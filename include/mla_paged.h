@@ -85,6 +85,7 @@ typedef enum {
 #define MLA_ROPE_DIM 64      /* rotary part of the query and of the cache entry */
 #define MLA_MAX_APPEND 65536 /* new tokens per sequence in one mla_kv_append */
 #define MLA_MAX_FUSED_BATCH 1024 /* sequences for a decode that schedules itself */
+#define MLA_FP8_TOKEN_BYTES 656  /* one token of the FP8 latent cache (see mla_kv_quantize_fp8) */
 
 /*
  * Number of key-range partitions used for `num_cus` compute units
@@ -234,6 +235,43 @@ mla_status_t mla_kv_append(void* kv_cache, int32_t num_pages, int32_t* block_tab
                            int32_t max_pages, int32_t* cache_seqlens, int32_t batch,
                            const void* new_kv, int32_t n_new, const int32_t* free_pages,
                            int32_t* free_count, int32_t* status, hipStream_t stream);
+
+/*
+ * FP8 latent cache (an extension: the DeepSeek-V3 hardware paper summary,
+ * section on FP8 mixed precision, applies FP8 to matrix products, training
+ * and communication, not to this cache).  Converts a bf16 cache
+ * kv_cache [num_pages][64][576] (device) into kv_fp8 [num_pages][64][656]
+ * bytes (device, caller-allocated), one record per token:
+ *   bytes [0, 512)    the 512 latent values as OCP E4M3 codes,
+ *   bytes [512, 528)  four float32 scales 2^e, one per 128 latent values,
+ *   bytes [528, 656)  the 64 rotary values, bf16, unchanged.
+ * A block's e is the smallest integer with max|x| <= 448 * 2^e (0 for an
+ * all-zero block); each value becomes the E4M3 code nearest to x * 2^-e,
+ * ties to the even code, with the sign of x.  code * 2^e is then exactly a
+ * bf16 value, so the decode over the FP8 cache equals the bf16 decode over
+ * the dequantized values.  Results for non-finite inputs are unspecified.
+ * Both pointers 16-byte aligned.  Errors: MLA_ERR_INVALID_ARGUMENT (null or
+ * misaligned pointer, num_pages <= 0), MLA_ERR_UNSUPPORTED (more than 2^31
+ * tokens), MLA_ERR_HIP.
+ */
+mla_status_t mla_kv_quantize_fp8(const void* kv_cache, int32_t num_pages, void* kv_fp8,
+                                 hipStream_t stream);
+
+/*
+ * Decode over the FP8 latent cache written by mla_kv_quantize_fp8
+ * (kv_fp8 [num_pages][64][656] bytes); every other argument as for
+ * mla_decode_paged, and the same combine follows.  Each page is copied as
+ * is (41 KiB instead of 72 KiB) and converted in LDS into the bf16 tile the
+ * matrix products read.  At most 16 query rows per sequence (s_q * h_q <=
+ * 16) and tile_metadata required; other shapes return MLA_ERR_UNSUPPORTED.
+ */
+mla_status_t mla_decode_paged_fp8(const void* q, const void* kv_fp8, const int32_t* block_table,
+                                  const int32_t* cache_seqlens, int32_t batch, int32_t s_q,
+                                  int32_t h_q, int32_t num_pages, int32_t max_pages,
+                                  float softmax_scale, int32_t causal,
+                                  const int32_t* tile_metadata, int32_t* num_splits,
+                                  int32_t num_cus, void* workspace, size_t workspace_bytes,
+                                  void* out, float* lse, hipStream_t stream);
 
 /* Static, human-readable text of a status code. */
 const char* mla_status_string(mla_status_t status);

@@ -36,6 +36,10 @@ __all__ = [
     "kv_append",
     "schedules_in_decode",
     "prefers_in_decode",
+    "kv_quantize_fp8",
+    "decode_paged_fp8",
+    "mla_decode_fp8",
+    "FP8_TOKEN_BYTES",
 ]
 
 HEAD_DIM = 576
@@ -43,6 +47,7 @@ V_DIM = 512
 PAGE_SIZE = 64
 META_INTS = 8
 MAX_FUSED_BATCH = 1024  # sequences for a decode that schedules itself
+FP8_TOKEN_BYTES = 656  # one token of the FP8 latent cache
 NOPE_DIM = 128  # per-head query part before absorption; value head width
 ROPE_DIM = 64
 
@@ -94,6 +99,10 @@ def load_library() -> ctypes.CDLL:
     lib.mla_absorb_output.restype = ctypes.c_int
     lib.mla_kv_append.argtypes = [vp, i32, vp, i32, vp, i32, vp, i32, vp, vp, vp, vp]
     lib.mla_kv_append.restype = ctypes.c_int
+    lib.mla_kv_quantize_fp8.argtypes = [vp, i32, vp, vp]
+    lib.mla_kv_quantize_fp8.restype = ctypes.c_int
+    lib.mla_decode_paged_fp8.argtypes = list(lib.mla_decode_paged.argtypes)
+    lib.mla_decode_paged_fp8.restype = ctypes.c_int
     lib.mla_status_string.argtypes = [ctypes.c_int]
     lib.mla_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -163,8 +172,8 @@ def decode_paged(q: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Ten
                  out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
                  stream=None):
     """Decode (without the combine).  Returns ``(out, lse, workspace)``.  With
-    ``tile_metadata=None`` (at most 16 rows, at most 1024 sequences) the decode
-    schedules itself and writes ``num_splits``."""
+    ``tile_metadata=None`` (at most 1024 sequences) the decode schedules itself
+    and writes ``num_splits``."""
     _need(q, "q", torch.bfloat16, 4)
     _need(kv_cache, "kv_cache", torch.bfloat16, 3)
     _need(block_table, "block_table", torch.int32, 2)
@@ -188,6 +197,70 @@ def decode_paged(q: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Ten
         _ptr(tile_metadata), _ptr(num_splits), num_cus, _ptr(workspace),
         workspace.numel() * workspace.element_size(), _ptr(out), _ptr(lse), _stream(stream)))
     return out, lse, workspace
+
+
+def kv_quantize_fp8(kv_cache: torch.Tensor, out: Optional[torch.Tensor] = None,
+                    stream=None) -> torch.Tensor:
+    """bf16 cache [pages, 64, 576] -> FP8 records [pages, 64, 656] (uint8):
+    512 E4M3 latent codes, four float32 power-of-two block scales, the 64
+    rotary values in bf16."""
+    _need(kv_cache, "kv_cache", torch.bfloat16, 3)
+    if kv_cache.shape[1] != PAGE_SIZE or kv_cache.shape[2] != HEAD_DIM:
+        raise ValueError("kv_cache must be [pages,64,576]")
+    P = kv_cache.shape[0]
+    if out is None:
+        out = torch.empty((P, PAGE_SIZE, FP8_TOKEN_BYTES), dtype=torch.uint8, device=kv_cache.device)
+    if out.dtype != torch.uint8 or tuple(out.shape) != (P, PAGE_SIZE, FP8_TOKEN_BYTES) or \
+            not out.is_contiguous():
+        raise ValueError("out must be contiguous uint8 [pages,64,656]")
+    _check("mla_kv_quantize_fp8", load_library().mla_kv_quantize_fp8(
+        _ptr(kv_cache), P, _ptr(out), _stream(stream)))
+    return out
+
+
+def decode_paged_fp8(q: torch.Tensor, kv_fp8: torch.Tensor, block_table: torch.Tensor,
+                     cache_seqlens: torch.Tensor, softmax_scale: float, causal: bool,
+                     tile_metadata: torch.Tensor, num_splits: torch.Tensor, num_cus: int = 0,
+                     workspace: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                     lse: Optional[torch.Tensor] = None, stream=None):
+    """Decode over the FP8 cache (at most 16 rows per sequence; the schedule
+    from get_metadata).  Returns ``(out, lse, workspace)``; combine as usual."""
+    _need(q, "q", torch.bfloat16, 4)
+    _need(block_table, "block_table", torch.int32, 2)
+    _need(cache_seqlens, "cache_seqlens", torch.int32, 1)
+    if kv_fp8.dtype != torch.uint8 or kv_fp8.dim() != 3 or not kv_fp8.is_contiguous() or \
+            kv_fp8.shape[1] != PAGE_SIZE or kv_fp8.shape[2] != FP8_TOKEN_BYTES:
+        raise ValueError("kv_fp8 must be contiguous uint8 [pages,64,656]")
+    batch, s_q, h_q, d = q.shape
+    if d != HEAD_DIM:
+        raise ValueError("q must be [b,s_q,h_q,576]")
+    if block_table.shape[0] != batch or cache_seqlens.shape[0] != batch:
+        raise ValueError("block_table / cache_seqlens batch mismatch")
+    dev = q.device
+    if out is None:
+        out = torch.empty((batch, s_q, h_q, V_DIM), dtype=torch.bfloat16, device=dev)
+    if lse is None:
+        lse = torch.empty((batch, s_q, h_q), dtype=torch.float32, device=dev)
+    need = workspace_bytes(batch, s_q, h_q, num_cus)
+    if workspace is None:
+        workspace = torch.empty((max(need, 16),), dtype=torch.uint8, device=dev)
+    _check("mla_decode_paged_fp8", load_library().mla_decode_paged_fp8(
+        _ptr(q), _ptr(kv_fp8), _ptr(block_table), _ptr(cache_seqlens), batch, s_q, h_q,
+        kv_fp8.shape[0], block_table.shape[1], float(softmax_scale), int(bool(causal)),
+        _ptr(tile_metadata), _ptr(num_splits), num_cus, _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _ptr(out), _ptr(lse), _stream(stream)))
+    return out, lse, workspace
+
+
+def mla_decode_fp8(q, kv_fp8, block_table, cache_seqlens, softmax_scale, causal, num_cus: int = 0,
+                   stream=None):
+    """One full decode step over the FP8 cache: schedule, decode, combine."""
+    batch, s_q, h_q, _ = q.shape
+    meta, splits = get_metadata(cache_seqlens, s_q, h_q, num_cus, stream)
+    out, lse, ws = decode_paged_fp8(q, kv_fp8, block_table, cache_seqlens, softmax_scale, causal,
+                                    meta, splits, num_cus, stream=stream)
+    combine(ws, splits, batch, s_q, h_q, out, lse, num_cus, stream)
+    return out, lse
 
 
 def combine(workspace: torch.Tensor, num_splits: torch.Tensor, batch: int, s_q: int, h_q: int,

@@ -83,6 +83,9 @@ extern "C" hipError_t mla_launch_decode(const mla::DecodeParams* prm, int rows_v
                                         hipStream_t stream);
 extern "C" hipError_t mla_launch_decode_sv64(const mla::DecodeParams* prm, hipStream_t stream);
 extern "C" hipError_t mla_launch_decode_t16(const mla::DecodeParams* prm, hipStream_t stream);
+extern "C" hipError_t mla_launch_decode_t16_fp8(const mla::DecodeParams* prm, hipStream_t stream);
+extern "C" hipError_t mla_launch_kv_quantize_fp8(const uint16_t* kv, int n_tokens, uint8_t* out,
+                                                 hipStream_t stream);
 extern "C" hipError_t mla_launch_combine(const float* o_acc, const float* lse_acc,
                                          const int32_t* splits, int batch, int R, uint16_t* out,
                                          float* lse, int wide, hipStream_t stream);
@@ -129,7 +132,9 @@ mla_status_t mla_get_metadata(const int32_t* cache_seqlens, int32_t batch, int32
   return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 
-mla_status_t mla_decode_paged(const void* q, const void* kv_cache, const int32_t* block_table,
+}  // extern "C"
+
+static mla_status_t decode_impl(bool fp8, const void* q, const void* kv_cache, const int32_t* block_table,
                               const int32_t* cache_seqlens, int32_t batch, int32_t s_q,
                               int32_t h_q, int32_t num_pages, int32_t max_pages,
                               float softmax_scale, int32_t causal, const int32_t* tile_metadata,
@@ -151,6 +156,8 @@ mla_status_t mla_decode_paged(const void* q, const void* kv_cache, const int32_t
   // without tile_metadata the decode schedules itself: at most
   // MLA_MAX_FUSED_BATCH sequences, and a block table small enough that its
   // schedule units fit 32-bit arithmetic
+  // the FP8 cache: workgroups of at most 16 rows, tile_metadata required
+  if (fp8 && (rows_variant_of(R) != 16 || !tile_metadata)) return MLA_ERR_UNSUPPORTED;
   if (!tile_metadata && (batch > MLA_MAX_FUSED_BATCH ||
                          (long long)batch * ((long long)max_pages + 2) >= (1LL << 30)))
     return MLA_ERR_UNSUPPORTED;
@@ -177,9 +184,45 @@ mla_status_t mla_decode_paged(const void* q, const void* kv_cache, const int32_t
   prm.scale_log2 = (float)((double)softmax_scale * 1.4426950408889634);
   prm.sched_c0 = fixed_cost_of(R);
   const int variant = rows_variant_of(R);
-  hipError_t e = variant == 64   ? mla_launch_decode_sv64(&prm, stream)
+  hipError_t e = fp8             ? mla_launch_decode_t16_fp8(&prm, stream)
+                 : variant == 64 ? mla_launch_decode_sv64(&prm, stream)
                  : variant == 16 ? mla_launch_decode_t16(&prm, stream)
                                  : mla_launch_decode(&prm, variant, stream);
+  return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+extern "C" {
+
+mla_status_t mla_decode_paged(const void* q, const void* kv_cache, const int32_t* block_table,
+                              const int32_t* cache_seqlens, int32_t batch, int32_t s_q,
+                              int32_t h_q, int32_t num_pages, int32_t max_pages,
+                              float softmax_scale, int32_t causal, const int32_t* tile_metadata,
+                              int32_t* num_splits, int32_t num_cus, void* workspace,
+                              size_t workspace_bytes, void* out, float* lse, hipStream_t stream) {
+  return decode_impl(false, q, kv_cache, block_table, cache_seqlens, batch, s_q, h_q, num_pages,
+                     max_pages, softmax_scale, causal, tile_metadata, num_splits, num_cus,
+                     workspace, workspace_bytes, out, lse, stream);
+}
+
+mla_status_t mla_decode_paged_fp8(const void* q, const void* kv_fp8, const int32_t* block_table,
+                                  const int32_t* cache_seqlens, int32_t batch, int32_t s_q,
+                                  int32_t h_q, int32_t num_pages, int32_t max_pages,
+                                  float softmax_scale, int32_t causal,
+                                  const int32_t* tile_metadata, int32_t* num_splits,
+                                  int32_t num_cus, void* workspace, size_t workspace_bytes,
+                                  void* out, float* lse, hipStream_t stream) {
+  return decode_impl(true, q, kv_fp8, block_table, cache_seqlens, batch, s_q, h_q, num_pages,
+                     max_pages, softmax_scale, causal, tile_metadata, num_splits, num_cus,
+                     workspace, workspace_bytes, out, lse, stream);
+}
+
+mla_status_t mla_kv_quantize_fp8(const void* kv_cache, int32_t num_pages, void* kv_fp8,
+                                 hipStream_t stream) {
+  if (!kv_cache || !kv_fp8 || num_pages <= 0) return MLA_ERR_INVALID_ARGUMENT;
+  if (((uintptr_t)kv_cache | (uintptr_t)kv_fp8) & 15) return MLA_ERR_INVALID_ARGUMENT;
+  if ((long long)num_pages * MLA_PAGE_SIZE > 0x7FFFFFFFLL) return MLA_ERR_UNSUPPORTED;
+  hipError_t e = mla_launch_kv_quantize_fp8((const uint16_t*)kv_cache, num_pages * MLA_PAGE_SIZE,
+                                            (uint8_t*)kv_fp8, stream);
   return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 

@@ -31,7 +31,31 @@ constexpr int kKS = kD / 32;  // 18 k-steps of the score product
 constexpr int kCT = 8;        // 16-column tiles per wave (128 columns)
 }  // namespace t16
 
-template <bool kFused>
+// FP8 latent cache: per token 512 E4M3 codes, four float32 power-of-two
+// scales (one per 128 latent values), the 64 rotary values in bf16.
+constexpr int kF8TokenBytes = 656;
+constexpr int kF8PageBytes = kPage * kF8TokenBytes;  // 41984 = 41 KiB
+constexpr int kF8Copies = kF8PageBytes / 1024;       // 41 wave-wide copies per page
+
+// FP8 page copy k (0 .. 40): a straight copy, lane l moving bytes
+// 1024 k + 16 l of the page (the whole offset in voffset, so the range check
+// of a resource sized to the live tokens covers it).
+__device__ __forceinline__ void f8_copy(MLA_LDS char* buf, __amdgpu_buffer_rsrc_t rs, int k,
+                                        int lane) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (MLA_LDS void*)(buf + 1024 * k), 16,
+                                           1024 * k + 16 * lane, 0, 0, 0);
+}
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t f8_resource(const char* page, int live) {
+  const int n = live < kPage ? live : kPage;
+  return __builtin_amdgcn_make_buffer_rsrc((void*)page, (short)0, n * kF8TokenBytes, kBufferFlags);
+}
+
+// kFused: no tile_metadata, every workgroup schedules itself.  kFp8: the
+// cache holds FP8 records; each page is copied as is into one of two FP8
+// buffers and converted into the bf16 tile the products read (the
+// dequantized values are exact bf16 values), so everything after the
+// conversion is the bf16 kernel.
+template <bool kFused, bool kFp8>
 __global__ void __launch_bounds__(kThreads, 1)
     decode_kernel_t16(const DecodeParams prm, const uint16_t* __restrict__ q_ptr,
                       const uint16_t* __restrict__ kv_ptr, const int32_t* __restrict__ block_table,
@@ -41,7 +65,7 @@ __global__ void __launch_bounds__(kThreads, 1)
                       float* __restrict__ lse_acc) {
   using namespace t16;
   __shared__ __attribute__((aligned(1024))) char tile0_[kTileBytes];
-  __shared__ __attribute__((aligned(1024))) char tile1_[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) char tile1_[kFp8 ? 2 * kF8PageBytes : kTileBytes];
   __shared__ __attribute__((aligned(16))) bf16x8 pbuf[2][64];  // [32-token k-step][lane]
   __shared__ float mx_buf[kWaves][16];                          // [wave][row]: tile max
   __shared__ float stat_l[kWaves][16];                          // [wave][row]: weight sums
@@ -137,11 +161,20 @@ __global__ void __launch_bounds__(kThreads, 1)
     });
   };
 
+  // all copies of one page into `tile` (bf16) or an FP8 buffer
+  auto issue_page = [&](MLA_LDS char* tile, int phys, int live) __attribute__((always_inline)) {
+    if constexpr (kFp8) {
+      const __amdgpu_buffer_rsrc_t rs = f8_resource(kvbase + (size_t)phys * kF8PageBytes, live);
+      for (int k = wave; k < kF8Copies; k += kWaves) f8_copy(tile, rs, k, lane);
+    } else {
+      loader.issue(tile, kvbase + (size_t)phys * kTileBytes, live, wave);
+    }
+  };
   auto load_item = [&](MLA_LDS char* tile, Item it) __attribute__((always_inline)) -> bool {
     const int L_it = uni(seqlens[it.b]);
     if (it.j * kPage >= L_it) return false;
     const int phys = uni(block_table[(size_t)it.b * prm.max_pages + it.j]);
-    loader.issue(tile, kvbase + (size_t)phys * kTileBytes, L_it - it.j * kPage, wave);
+    issue_page(tile, phys, L_it - it.j * kPage);
     return true;
   };
 
@@ -154,7 +187,10 @@ __global__ void __launch_bounds__(kThreads, 1)
       const int L_it = uni(seqlens[it.b]);
       if (it.j * kPage < L_it) {
         const int phys = uni(block_table[(size_t)it.b * prm.max_pages + it.j]);
-        cp.rsrc = PageLoader::resource(kvbase + (size_t)phys * kTileBytes, L_it - it.j * kPage);
+        if constexpr (kFp8)
+          cp.rsrc = f8_resource(kvbase + (size_t)phys * kF8PageBytes, L_it - it.j * kPage);
+        else
+          cp.rsrc = PageLoader::resource(kvbase + (size_t)phys * kTileBytes, L_it - it.j * kPage);
         cp.valid = true;
       }
     }
@@ -199,9 +235,17 @@ __global__ void __launch_bounds__(kThreads, 1)
     static_for<0, kKS>([&](auto ksc) __attribute__((always_inline)) {
       constexpr int ks = decltype(ksc)::value;
       if constexpr (ks + DK < kKS) kr[(ks + DK) % (DK + 1)] = load_k(ks + DK);
-      // the next page's 18 copy instructions, one per k-step
+      // the next page's copy instructions, one per k-step (18 per wave for
+      // a bf16 page; 11 or 10 of the 41 for an FP8 page)
       static_assert(kKS == kLoadsPerWave, "one copy per k-step");
-      if (cp.valid) loader.issue_one(cp.tile, cp.rsrc, wave, ks);
+      if constexpr (kFp8) {
+        if constexpr (kWaves * ks < kF8Copies + kWaves) {
+          if (cp.valid && wave + kWaves * ks < kF8Copies)
+            f8_copy(cp.tile, cp.rsrc, wave + kWaves * ks, lane);
+        }
+      } else {
+        if (cp.valid) loader.issue_one(cp.tile, cp.rsrc, wave, ks);
+      }
       s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kr[ks % (DK + 1)], qf[ks], s, 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
     });
@@ -303,6 +347,36 @@ __global__ void __launch_bounds__(kThreads, 1)
     split_idx = 0;  // later sequences of this partition start at their page 0
   };
 
+  // FP8 page (64 records of 656 bytes) -> the bf16 tile: item (t, c) is
+  // 16-byte chunk c of token t, 8 latent values converted with their
+  // block's scale (exact: the scale is a power of two) or 8 rotary values
+  // copied; stored at the tile's swizzled chunk c ^ (t & 7).  Tokens past
+  // the live ones arrived as zeros and convert to zeros.
+  auto convert_page = [&](MLA_LDS char* f8) __attribute__((always_inline)) {
+    typedef __attribute__((ext_vector_type(2))) __bf16 bf2;
+#pragma unroll 6
+    for (int u = 0; u < kPage * kChunksPerRow / kThreads; ++u) {  // 18
+      const int i = threadIdx.x + kThreads * u;
+      const int t = i / kChunksPerRow;
+      const int c = i - kChunksPerRow * t;
+      MLA_LDS char* rec = f8 + t * kF8TokenBytes;
+      i32x4 v;
+      if (c < kDv / 8) {
+        const i32x2 w = *(MLA_LDS i32x2*)(rec + 8 * c);
+        const float sc = *(MLA_LDS float*)(rec + kDv + 4 * (c >> 4));
+        const bf2 a0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((unsigned)w[0], sc, false);
+        const bf2 a1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((unsigned)w[0], sc, true);
+        const bf2 a2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((unsigned)w[1], sc, false);
+        const bf2 a3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((unsigned)w[1], sc, true);
+        v = i32x4{__builtin_bit_cast(int, a0), __builtin_bit_cast(int, a1),
+                  __builtin_bit_cast(int, a2), __builtin_bit_cast(int, a3)};
+      } else {
+        v = *(MLA_LDS i32x4*)(rec + kDv + 16 + 16 * (c - kDv / 8));
+      }
+      *(MLA_LDS i32x4*)(tile0 + t * kRowBytes + 16 * (c ^ swz(t))) = v;
+    }
+  };
+
   // One step: compute `cur` from tile A while the next page streams into B.
   auto step = [&](MLA_LDS char* tA, MLA_LDS char* tB) __attribute__((always_inline)) -> bool {
     const Item nx = advance(cur);
@@ -313,9 +387,19 @@ __global__ void __launch_bounds__(kThreads, 1)
     __builtin_amdgcn_s_waitcnt(kWaitVm0);  // this wave's part of tile A landed
     __syncthreads();                       // ... and every wave's; B is free
     if (cur.j * kPage < L) {
-      compute_page(tA, cur.j, cp);
+      if constexpr (kFp8) {
+        convert_page(tA);  // A (FP8) -> the bf16 tile, free since the barrier
+        __syncthreads();
+        compute_page(tile0, cur.j, cp);
+      } else {
+        compute_page(tA, cur.j, cp);
+      }
     } else if (cp.valid) {
-      for (int i = 0; i < kLoadsPerWave; ++i) loader.issue_one(cp.tile, cp.rsrc, wave, i);
+      if constexpr (kFp8) {
+        for (int k = wave; k < kF8Copies; k += kWaves) f8_copy(cp.tile, cp.rsrc, k, lane);
+      } else {
+        for (int i = 0; i < kLoadsPerWave; ++i) loader.issue_one(cp.tile, cp.rsrc, wave, i);
+      }
     }
     if (!has_next || nx.b != cur.b) {
       finish_segment(cur.b);
@@ -325,18 +409,21 @@ __global__ void __launch_bounds__(kThreads, 1)
     return has_next;
   };
 
+  // page buffers: the two bf16 tiles, or two FP8 buffers (the bf16 tile
+  // then only receives conversions)
+  MLA_LDS char* bufA = kFp8 ? tile1 : tile0;
+  MLA_LDS char* bufB = kFp8 ? tile1 + kF8PageBytes : tile1;
   if constexpr (kFused) {
     // length and page of the first item were read with the schedule
     begin_segment(cur.b, L0);
-    if (cur.j * kPage < L0)
-      loader.issue(tile0, kvbase + (size_t)phys0 * kTileBytes, L0 - cur.j * kPage, wave);
+    if (cur.j * kPage < L0) issue_page(bufA, phys0, L0 - cur.j * kPage);
   } else {
     begin_segment(cur.b, uni(seqlens[cur.b]));
-    load_item(tile0, cur);
+    load_item(bufA, cur);
   }
   while (true) {
-    if (!step(tile0, tile1)) break;
-    if (!step(tile1, tile0)) break;
+    if (!step(bufA, bufB)) break;
+    if (!step(bufB, bufA)) break;
   }
 }
 
@@ -346,12 +433,24 @@ extern "C" hipError_t mla_launch_decode_t16(const mla::DecodeParams* prm, hipStr
   using namespace mla;
   const int groups = (prm->num_parts + 7) / 8;
   if (prm->meta != nullptr)
-    hipLaunchKernelGGL(decode_kernel_t16<false>, dim3(groups * 8), dim3(kThreads), 0, stream, *prm,
+    hipLaunchKernelGGL((decode_kernel_t16<false, false>), dim3(groups * 8), dim3(kThreads), 0, stream, *prm,
                        prm->q, prm->kv, prm->block_table, prm->seqlens, prm->meta,
                        prm->splits, prm->out, prm->lse, prm->o_acc, prm->lse_acc);
   else  // schedule inside the launch (batch <= kFusedMaxBatch, checked by the caller)
-    hipLaunchKernelGGL(decode_kernel_t16<true>, dim3(groups * 8), dim3(kThreads), 0, stream, *prm,
+    hipLaunchKernelGGL((decode_kernel_t16<true, false>), dim3(groups * 8), dim3(kThreads), 0, stream, *prm,
                        prm->q, prm->kv, prm->block_table, prm->seqlens, prm->meta,
                        prm->splits, prm->out, prm->lse, prm->o_acc, prm->lse_acc);
+  return hipGetLastError();
+}
+
+// FP8 latent cache (<= 16 rows per sequence; tile_metadata required: the two
+// FP8 buffers and the bf16 tile leave no LDS for the in-launch schedule).
+extern "C" hipError_t mla_launch_decode_t16_fp8(const mla::DecodeParams* prm, hipStream_t stream) {
+  using namespace mla;
+  if (prm->meta == nullptr) return hipErrorInvalidValue;
+  const int groups = (prm->num_parts + 7) / 8;
+  hipLaunchKernelGGL((decode_kernel_t16<false, true>), dim3(groups * 8), dim3(kThreads), 0, stream,
+                     *prm, prm->q, prm->kv, prm->block_table, prm->seqlens, prm->meta,
+                     prm->splits, prm->out, prm->lse, prm->o_acc, prm->lse_acc);
   return hipGetLastError();
 }

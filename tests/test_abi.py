@@ -175,3 +175,19 @@ def test_schedule_policy_of_the_binding():
     assert m.prefers_in_decode(8, 1, 16, 64)
     assert not m.prefers_in_decode(8, 2, 16, 64)              # 32 rows: separate launch
     assert not m.prefers_in_decode(2000, 1, 16, 64)
+
+
+def test_fp8_entry_points_reject_bad_arguments(lib):
+    null = ctypes.c_void_p(0)
+    one = ctypes.c_void_p(16)
+    assert lib.mla_kv_quantize_fp8(null, 4, one, null) == 1
+    assert lib.mla_kv_quantize_fp8(one, 4, ctypes.c_void_p(24), null) == 1  # misaligned
+    assert lib.mla_kv_quantize_fp8(one, 0, one, null) == 1
+    assert lib.mla_kv_quantize_fp8(one, 1 << 26, one, null) == 2            # 2^32 tokens
+    args = [one, one, one, one, 4, 1, 16, 10, 4, 0.1, 0, one, one, 8, one, 10 ** 9, one, one, null]
+    bad = list(args); bad[6] = 32                                            # 32 rows
+    assert lib.mla_decode_paged_fp8(*bad) == 2
+    bad = list(args); bad[11] = null                                         # no tile_metadata
+    assert lib.mla_decode_paged_fp8(*bad) == 2
+    bad = list(args); bad[1] = null
+    assert lib.mla_decode_paged_fp8(*bad) == 1
