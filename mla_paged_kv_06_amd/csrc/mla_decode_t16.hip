@@ -136,7 +136,9 @@ __global__ void __launch_bounds__(kThreads, 1)
   PageLoader loader;
   loader.init(lane);
 
-  auto begin_segment = [&](int b, int Lb) __attribute__((always_inline)) {
+  // load_q: the query rows come by global loads (every segment but the
+  // partition's first, whose rows are staged in LDS; see below)
+  auto begin_segment = [&](int b, int Lb, bool load_q) __attribute__((always_inline)) {
     L = Lb;
     if constexpr (kFused) {
       seg_s_lo = uni(split_of<kThreads>(sched_sh, b, prm.batch));
@@ -147,7 +149,7 @@ __global__ void __launch_bounds__(kThreads, 1)
     }
     // rows past R read row 0 and are never stored; they see no tokens
     const uint16_t* qrow = q_ptr + ((size_t)b * prm.R + (row_live ? l16 : 0)) * kD + 8 * g;
-    static_for<0, kKS>([&](auto kc) __attribute__((always_inline)) {
+    if (load_q) static_for<0, kKS>([&](auto kc) __attribute__((always_inline)) {
       qf[decltype(kc)::value] = *(const bf16x8*)(qrow + 32 * decltype(kc)::value);
     });
     const int i = (row_live ? l16 : 0) / prm.h_q;
@@ -378,7 +380,12 @@ __global__ void __launch_bounds__(kThreads, 1)
   };
 
   // One step: compute `cur` from tile A while the next page streams into B.
-  auto step = [&](MLA_LDS char* tA, MLA_LDS char* tB) __attribute__((always_inline)) -> bool {
+  // kFirst: the partition's first step, whose query rows wait in B (staged
+  // there with the first page's copies): read into registers, then one more
+  // barrier before the next page's copies overwrite B
+  auto step = [&](MLA_LDS char* tA, MLA_LDS char* tB, auto first_c) __attribute__((always_inline))
+      -> bool {
+    constexpr bool kFirst = decltype(first_c)::value;
     const Item nx = advance(cur);
     const bool has_next = item_before(nx, eb, ej);
     // descriptor of the next copy first: its scalar loads (block table and
@@ -386,6 +393,18 @@ __global__ void __launch_bounds__(kThreads, 1)
     PendingCopy cp = next_copy(tB, nx, has_next);
     __builtin_amdgcn_s_waitcnt(kWaitVm0);  // this wave's part of tile A landed
     __syncthreads();                       // ... and every wave's; B is free
+    if constexpr (kFirst) {
+      // row l16 of the staged query, in the page layout: the K fragment's
+      // addressing with token l16
+      const int q_lane = l16 * kRowBytes + 16 * (g ^ (sw & 3));
+      const int q_even = q_lane + ((sw & 4) ? 64 : 0);
+      const int q_odd = q_lane - ((sw & 4) ? 64 : 0);
+      static_for<0, kKS>([&](auto kc) __attribute__((always_inline)) {
+        constexpr int ks = decltype(kc)::value;
+        qf[ks] = *(MLA_LDS bf16x8*)(tB + ((ks & 1) ? q_odd : q_even) + 64 * ks);
+      });
+      lds_barrier();
+    }
     if (cur.j * kPage < L) {
       if constexpr (kFp8) {
         convert_page(tA);  // A (FP8) -> the bf16 tile, free since the barrier
@@ -403,7 +422,7 @@ __global__ void __launch_bounds__(kThreads, 1)
     }
     if (!has_next || nx.b != cur.b) {
       finish_segment(cur.b);
-      if (has_next) begin_segment(nx.b, uni(seqlens[nx.b]));
+      if (has_next) begin_segment(nx.b, uni(seqlens[nx.b]), true);
     }
     cur = nx;
     return has_next;
@@ -413,17 +432,31 @@ __global__ void __launch_bounds__(kThreads, 1)
   // then only receives conversions)
   MLA_LDS char* bufA = kFp8 ? tile1 : tile0;
   MLA_LDS char* bufB = kFp8 ? tile1 + kF8PageBytes : tile1;
+  // The first segment's query rows (R <= 16, rows past R arrive as zeros
+  // and see no tokens) are staged in B by two waves' 9 copies each, in the
+  // page layout, instead of 18 global loads in every wave: a quarter of the
+  // bytes through the CU's address path ahead of the first page.
+  {
+    const __amdgpu_buffer_rsrc_t qrs =
+        PageLoader::resource((const char*)(q_ptr + (size_t)cur.b * prm.R * kD), prm.R);
+    if (wave < 2) {
+#pragma unroll
+      for (int i = 0; i < 9; ++i) loader.issue_one(bufB, qrs, wave, i);
+    }
+  }
   if constexpr (kFused) {
     // length and page of the first item were read with the schedule
-    begin_segment(cur.b, L0);
+    begin_segment(cur.b, L0, false);
     if (cur.j * kPage < L0) issue_page(bufA, phys0, L0 - cur.j * kPage);
   } else {
-    begin_segment(cur.b, uni(seqlens[cur.b]));
+    begin_segment(cur.b, uni(seqlens[cur.b]), false);
     load_item(bufA, cur);
   }
-  while (true) {
-    if (!step(bufA, bufB)) break;
-    if (!step(bufB, bufA)) break;
+  if (step(bufA, bufB, std::true_type{})) {
+    while (true) {
+      if (!step(bufB, bufA, std::false_type{})) break;
+      if (!step(bufA, bufB, std::false_type{})) break;
+    }
   }
 }
 
