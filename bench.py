@@ -689,11 +689,13 @@ def main():
             "absorption": absorption_rates(mla, b, s_q, h_q, 2000 + k, dev),
             "kv_append": kv_append_rates(mla, [int(x) for x in case.cache_seqlens], s_q, 3000 + k,
                                          dev),
-            # more query tokens per sequence: 4 speculative tokens on the
-            # memory-bound workload's sequences, and a 512-token chunk at
-            # 128 heads over a 4096-token cache
+            # more query tokens per sequence: 2 and 4 speculative tokens on
+            # the memory-bound workload's sequences (32 and 64 rows), and a
+            # 512-token chunk at 128 heads over a 4096-token cache
             "fp8_cache": fp8_cache_rates(mla, case, dev),
             "query_tokens": {
+                "speculative_s_q2": query_token_rates(
+                    mla, [int(x) for x in make_config_case(2).cache_seqlens], 2, 16, 4001, dev),
                 "speculative_s_q4": query_token_rates(
                     mla, [int(x) for x in make_config_case(2).cache_seqlens], 4, 16, 4002, dev),
                 "chunk_512x128": query_token_rates(mla, [4096], 512, 128, 4003, dev),

@@ -150,7 +150,9 @@ __global__ void __launch_bounds__(kThreads, 1)
   PageLoader loader;
   loader.init(lane);
 
-  auto begin_segment = [&](int b, int Lb) __attribute__((always_inline)) {
+  // load_q: the query rows come by global loads (every segment but the
+  // partition's first, whose rows are staged in LDS; see below)
+  auto begin_segment = [&](int b, int Lb, bool load_q) __attribute__((always_inline)) {
     L = Lb;
     if constexpr (kFused) {
       seg_s_lo = uni(split_of<kThreads>(sched_sh, b, prm.batch));
@@ -166,7 +168,7 @@ __global__ void __launch_bounds__(kThreads, 1)
       // rows past R read row 0 and are never stored; they see no tokens, so
       // their weights are exactly 0
       const uint16_t* qrow = q_ptr + ((size_t)b * prm.R + (live ? row : 0)) * kD + 8 * g;
-      static_for<0, KS>([&](auto kc) __attribute__((always_inline)) {
+      if (load_q) static_for<0, KS>([&](auto kc) __attribute__((always_inline)) {
         constexpr int ks = decltype(kc)::value;
         qf[rt][ks] = *(const bf16x8*)(qrow + 32 * ks);
       });
@@ -391,7 +393,12 @@ __global__ void __launch_bounds__(kThreads, 1)
   // before its first page, so the wait at the top of the step (needed for
   // the page anyway) also covers them and no load into registers is ever
   // pending next to a page copy.
-  auto step = [&](MLA_LDS char* tA, MLA_LDS char* tB) __attribute__((always_inline)) -> bool {
+  // kFirst: the partition's first step, whose query rows wait in B (staged
+  // there with the first page's copies): read into registers, then one more
+  // barrier before the next page's copies overwrite B
+  auto step = [&](MLA_LDS char* tA, MLA_LDS char* tB, auto first_c) __attribute__((always_inline))
+      -> bool {
+    constexpr bool kFirst = decltype(first_c)::value;
     const Item nx = advance(cur);
     const bool has_next = item_before(nx, eb, ej);
     // descriptor of the next copy first: its scalar loads (block table and
@@ -399,6 +406,19 @@ __global__ void __launch_bounds__(kThreads, 1)
     PendingCopy cp = next_copy(tB, nx, has_next);
     __builtin_amdgcn_s_waitcnt(kWaitVm0);  // this wave's part of tile A landed
     __syncthreads();                       // ... and every wave's; B is free
+    if constexpr (kFirst) {
+      // row 16 rt + l16 of the staged query, in the page layout: the K
+      // fragment's addressing with token 16 rt + l16 (same swizzle)
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) {
+        static_for<0, KS>([&](auto kc) __attribute__((always_inline)) {
+          constexpr int ks = decltype(kc)::value;
+          qf[rt][ks] = *(MLA_LDS bf16x8*)(tB + 16 * rt * kRowBytes +
+                                          ((ks & 1) ? k_odd : k_even) + 64 * ks);
+        });
+      }
+      lds_barrier();
+    }
     const bool has_tokens = cur.j * kPage < L;
     if (has_tokens) {
       compute_page(tA, cur.j, cp);
@@ -407,24 +427,36 @@ __global__ void __launch_bounds__(kThreads, 1)
     }
     if (!has_next || nx.b != cur.b) {
       finish_segment(cur.b);
-      if (has_next) begin_segment(nx.b, uni(seqlens[nx.b]));
+      if (has_next) begin_segment(nx.b, uni(seqlens[nx.b]), true);
     }
     cur = nx;
     return has_next;
   };
 
+  // The first segment's query rows (R <= 32; rows past R arrive as zeros
+  // and see no tokens) are staged in tile 1, each wave copying one 8-row
+  // block, instead of all 32 rows loaded by every wave.
+  {
+    static_assert(RT * 16 <= 4 * 8, "four 8-row blocks");
+    const __amdgpu_buffer_rsrc_t qrs =
+        PageLoader::resource((const char*)(q_ptr + (size_t)cur.b * prm.R * kD), prm.R);
+#pragma unroll
+    for (int i = 0; i < 9; ++i) loader.issue_one(tile1, qrs, wave, i);
+  }
   if constexpr (kFused) {
     // length and page of the first item were read with the schedule
-    begin_segment(cur.b, L0);
+    begin_segment(cur.b, L0, false);
     if (cur.j * kPage < L0)
       loader.issue(tile0, kvbase + (size_t)phys0 * kTileBytes, L0 - cur.j * kPage, wave);
   } else {
-    begin_segment(cur.b, uni(seqlens[cur.b]));
+    begin_segment(cur.b, uni(seqlens[cur.b]), false);
     load_item(tile0, cur);
   }
-  while (true) {
-    if (!step(tile0, tile1)) break;
-    if (!step(tile1, tile0)) break;
+  if (step(tile0, tile1, std::true_type{})) {
+    while (true) {
+      if (!step(tile1, tile0, std::false_type{})) break;
+      if (!step(tile0, tile1, std::false_type{})) break;
+    }
   }
 }
 
