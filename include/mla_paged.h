@@ -99,9 +99,9 @@ int32_t mla_num_partitions(int32_t s_q, int32_t h_q, int32_t num_cus);
 size_t mla_metadata_ints(int32_t s_q, int32_t h_q, int32_t num_cus);
 
 /*
- * Bytes of workspace mla_decode_paged / mla_combine need: float32 partial
- * outputs and log-sum-exps for sequences whose keys are split over several
- * partitions, one slot per (sequence, split).  With a single partition
+ * Bytes of workspace mla_decode_paged / mla_combine need: bf16 normalized
+ * partial outputs and float32 log-sum-exps for sequences whose keys are
+ * split over several partitions, one slot per (sequence, split).  With a single partition
  * (s_q * h_q of 16384 rows or more on 256 CUs) nothing is split: 256 bytes,
  * never written, and mla_combine launches nothing.
  */
@@ -131,7 +131,7 @@ mla_status_t mla_get_metadata(const int32_t* cache_seqlens, int32_t batch, int32
  * Decode.  Each workgroup walks its partition's pages, streams every 64-token
  * latent page from HBM into LDS once, and runs Q.K^T and P.V on bf16 matrix
  * cores with an online softmax.  Sequences owned by one partition are
- * written straight to out/lse; the others write float32 partials into the
+ * written straight to out/lse; the others write bf16 partials into the
  * workspace for mla_combine.  tile_metadata and num_splits must come from
  * mla_get_metadata with the same cache_seqlens, batch, s_q, h_q and num_cus.
  * Alternatively, when batch <= MLA_MAX_FUSED_BATCH and

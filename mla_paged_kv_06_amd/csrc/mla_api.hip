@@ -64,12 +64,12 @@ int parts_of(int32_t s_q, int32_t h_q, int32_t num_cus) {
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-// workspace: o_acc [slots][R][512] fp32, then lse_acc [slots][R] fp32.  With
+// workspace: o_acc [slots][R][512] bf16, then lse_acc [slots][R] fp32.  With
 // one partition no sequence is split (it owns every unit), so no slot is
 // ever written; a token 256 bytes keep the pointer checks uniform.
 size_t slots_of(int batch, int parts) { return parts > 1 ? (size_t)batch + parts : 0; }
 size_t oacc_bytes(int batch, int R, int parts) {
-  return align_up(slots_of(batch, parts) * R * MLA_V_DIM * sizeof(float), 256);
+  return align_up(slots_of(batch, parts) * R * MLA_V_DIM * sizeof(uint16_t), 256);
 }
 size_t ws_bytes(int batch, int R, int parts) {
   const size_t n = oacc_bytes(batch, R, parts) +
@@ -86,7 +86,7 @@ extern "C" hipError_t mla_launch_decode_t16(const mla::DecodeParams* prm, hipStr
 extern "C" hipError_t mla_launch_decode_t16_fp8(const mla::DecodeParams* prm, hipStream_t stream);
 extern "C" hipError_t mla_launch_kv_quantize_fp8(const uint16_t* kv, int n_tokens, uint8_t* out,
                                                  hipStream_t stream);
-extern "C" hipError_t mla_launch_combine(const float* o_acc, const float* lse_acc,
+extern "C" hipError_t mla_launch_combine(const uint16_t* o_acc, const float* lse_acc,
                                          const int32_t* splits, int batch, int R, uint16_t* out,
                                          float* lse, int wide, hipStream_t stream);
 
@@ -171,7 +171,7 @@ static mla_status_t decode_impl(bool fp8, const void* q, const void* kv_cache, c
   prm.splits = num_splits;
   prm.out = (uint16_t*)out;
   prm.lse = lse;
-  prm.o_acc = (float*)workspace;
+  prm.o_acc = (uint16_t*)workspace;
   prm.lse_acc = (float*)((char*)workspace + oacc_bytes(batch, R, parts));
   prm.batch = batch;
   prm.s_q = s_q;
@@ -237,7 +237,7 @@ mla_status_t mla_combine(const void* workspace, size_t workspace_bytes, const in
   const int R = s_q * h_q;
   if (workspace_bytes < ws_bytes(batch, R, parts)) return MLA_ERR_WORKSPACE_TOO_SMALL;
   if (parts == 1) return MLA_OK;  // one partition: nothing was split
-  const float* o_acc = (const float*)workspace;
+  const uint16_t* o_acc = (const uint16_t*)workspace;
   const float* lse_acc = (const float*)((const char*)workspace + oacc_bytes(batch, R, parts));
   // many partitions per sequence on average: spread each row's partials over
   // a whole workgroup

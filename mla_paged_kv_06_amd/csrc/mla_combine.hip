@@ -19,7 +19,15 @@ __device__ __forceinline__ float lane_value(float v, int lane) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
 }
 
-__global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ o_acc,
+// 8 bf16 partial values (16 bytes) -> two float32 quadruples, exactly
+__device__ __forceinline__ void widen8(i32x4 r, f32x4& lo, f32x4& hi) {
+  lo = f32x4{__uint_as_float((unsigned)r[0] << 16), __uint_as_float((unsigned)r[0] & 0xFFFF0000u),
+             __uint_as_float((unsigned)r[1] << 16), __uint_as_float((unsigned)r[1] & 0xFFFF0000u)};
+  hi = f32x4{__uint_as_float((unsigned)r[2] << 16), __uint_as_float((unsigned)r[2] & 0xFFFF0000u),
+             __uint_as_float((unsigned)r[3] << 16), __uint_as_float((unsigned)r[3] & 0xFFFF0000u)};
+}
+
+__global__ void __launch_bounds__(256) combine_kernel(const uint16_t* __restrict__ o_acc,
                                                       const float* __restrict__ lse_acc,
                                                       const int32_t* __restrict__ splits, int R,
                                                       uint16_t* __restrict__ out,
@@ -33,16 +41,15 @@ __global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ 
   const int ns = __builtin_amdgcn_readfirstlane(splits[b + 1]) - s0;
   if (ns <= 1 || row >= R) return;  // uniform per wave; no block barrier below
   const float* lrow = lse_acc + (size_t)s0 * R + row;
-  const float* orow_acc = o_acc + ((size_t)s0 * R + row) * kDv + 8 * t;
-  f32x4 v[2 * U];
+  const uint16_t* orow_acc = o_acc + ((size_t)s0 * R + row) * kDv + 8 * t;
+  i32x4 v[U];  // raw bf16 partial values, widened where they are summed
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     if (u < ns) {
-      const float* src = orow_acc + (size_t)u * R * kDv;
-      v[2 * u] = *(const f32x4*)src;
-      v[2 * u + 1] = *(const f32x4*)(src + 4);
+      const uint16_t* src = orow_acc + (size_t)u * R * kDv;
+      v[u] = *(const i32x4*)src;
     } else {
-      v[2 * u] = v[2 * u + 1] = f32x4{0.f, 0.f, 0.f, 0.f};
+      v[u] = i32x4{0, 0, 0, 0};
     }
   }
   // split weights: lanes over splits, a wave max and sum
@@ -72,25 +79,28 @@ __global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ 
   for (int u = 0; u < U; ++u) {
     if (u < ns) {
       const float w = weight(u);
-      a0 += w * v[2 * u];
-      a1 += w * v[2 * u + 1];
+      f32x4 lo, hi;
+      widen8(v[u], lo, hi);
+      a0 += w * lo;
+      a1 += w * hi;
     }
   }
   for (int s = U; s < ns; s += U) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       if (s + u < ns) {
-        const float* src = orow_acc + (size_t)(s + u) * R * kDv;
-        v[2 * u] = *(const f32x4*)src;
-        v[2 * u + 1] = *(const f32x4*)(src + 4);
+        const uint16_t* src = orow_acc + (size_t)(s + u) * R * kDv;
+        v[u] = *(const i32x4*)src;
       }
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       if (s + u < ns) {
         const float w = weight(s + u);
-        a0 += w * v[2 * u];
-        a1 += w * v[2 * u + 1];
+        f32x4 lo, hi;
+        widen8(v[u], lo, hi);
+        a0 += w * lo;
+        a1 += w * hi;
       }
     }
   }
@@ -109,7 +119,7 @@ __global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ 
 // meet in LDS and each wave finishes 128 columns.
 constexpr int kWideUnroll = 8;  // partial rows in flight per wave
 
-__global__ void __launch_bounds__(256) combine_wide_kernel(const float* __restrict__ o_acc,
+__global__ void __launch_bounds__(256) combine_wide_kernel(const uint16_t* __restrict__ o_acc,
                                                            const float* __restrict__ lse_acc,
                                                            const int32_t* __restrict__ splits,
                                                            int R, uint16_t* __restrict__ out,
@@ -123,19 +133,18 @@ __global__ void __launch_bounds__(256) combine_wide_kernel(const float* __restri
   const int ns = __builtin_amdgcn_readfirstlane(splits[b + 1]) - s0;
   if (ns <= 1) return;  // uniform over the workgroup
   const float* lrow = lse_acc + (size_t)s0 * R + row;
-  const float* base = o_acc + ((size_t)s0 * R + row) * kDv + 8 * t;
+  const uint16_t* base = o_acc + ((size_t)s0 * R + row) * kDv + 8 * t;
   // this wave's first kWideUnroll partial rows (splits wv, wv + 4, ...) are
   // requested first: their loads overlap those of the lse values
-  f32x4 v[2 * kWideUnroll];
+  i32x4 v[kWideUnroll];  // raw bf16 partial values, widened where they are summed
 #pragma unroll
   for (int u = 0; u < kWideUnroll; ++u) {
     const int si = wv + kWaves * u;
     if (si < ns) {
-      const float* src = base + (size_t)si * R * kDv;
-      v[2 * u] = *(const f32x4*)src;
-      v[2 * u + 1] = *(const f32x4*)(src + 4);
+      const uint16_t* src = base + (size_t)si * R * kDv;
+      v[u] = *(const i32x4*)src;
     } else {
-      v[2 * u] = v[2 * u + 1] = f32x4{0.f, 0.f, 0.f, 0.f};
+      v[u] = i32x4{0, 0, 0, 0};
     }
   }
   // max and sum of the split weights (lanes over splits; every wave computes
@@ -170,9 +179,8 @@ __global__ void __launch_bounds__(256) combine_wide_kernel(const float* __restri
       for (int u = 0; u < kWideUnroll; ++u) {
         const int si = s + kWaves * u;
         if (si < ns) {
-          const float* src = base + (size_t)si * R * kDv;
-          v[2 * u] = *(const f32x4*)src;
-          v[2 * u + 1] = *(const f32x4*)(src + 4);
+          const uint16_t* src = base + (size_t)si * R * kDv;
+          v[u] = *(const i32x4*)src;
         }
       }
     }
@@ -181,8 +189,10 @@ __global__ void __launch_bounds__(256) combine_wide_kernel(const float* __restri
       const int si = s + kWaves * u;
       if (si < ns) {
         const float w = weight(si);
-        a0 += w * v[2 * u];
-        a1 += w * v[2 * u + 1];
+        f32x4 lo, hi;
+        widen8(v[u], lo, hi);
+        a0 += w * lo;
+        a1 += w * hi;
       }
     }
   }
@@ -208,7 +218,7 @@ __global__ void __launch_bounds__(256) combine_wide_kernel(const float* __restri
 
 // wide: the caller's estimate that sequences are split many ways (partitions
 // well above the batch); the result is the same either way.
-extern "C" hipError_t mla_launch_combine(const float* o_acc, const float* lse_acc,
+extern "C" hipError_t mla_launch_combine(const uint16_t* o_acc, const float* lse_acc,
                                          const int32_t* splits, int batch, int R, uint16_t* out,
                                          float* lse, int wide, hipStream_t stream) {
   if (wide) {

@@ -61,7 +61,7 @@ __global__ void __launch_bounds__(kThreads, 1)
                       const uint16_t* __restrict__ kv_ptr, const int32_t* __restrict__ block_table,
                       const int32_t* __restrict__ seqlens, const int32_t* __restrict__ meta,
                       int32_t* __restrict__ splits, uint16_t* __restrict__ out_ptr,
-                      float* __restrict__ lse_ptr, float* __restrict__ o_acc,
+                      float* __restrict__ lse_ptr, uint16_t* __restrict__ o_acc,
                       float* __restrict__ lse_acc) {
   using namespace t16;
   __shared__ __attribute__((aligned(1024))) char tile0_[kTileBytes];
@@ -339,10 +339,14 @@ __global__ void __launch_bounds__(kThreads, 1)
           *(bf16x4*)(orow + 16 * ct) = bf16x4{a[0], a[1], c[0], c[1]};
         });
       } else {
-        float* orow = o_acc + ((size_t)slot * prm.R + l16) * kDv + col_base + 4 * g;
+        // the normalized partial, rounded to bf16 like the output
+        uint16_t* orow = o_acc + ((size_t)slot * prm.R + l16) * kDv + col_base + 4 * g;
         static_for<0, kCT>([&](auto cc) __attribute__((always_inline)) {
           constexpr int ct = decltype(cc)::value;
-          *(f32x4*)(orow + 16 * ct) = o[ct] * inv;
+          const f32x4 v = o[ct] * inv;
+          const bf16x2 a = to_bf16x2(v[0], v[1]);
+          const bf16x2 c = to_bf16x2(v[2], v[3]);
+          *(bf16x4*)(orow + 16 * ct) = bf16x4{a[0], a[1], c[0], c[1]};
         });
       }
     }

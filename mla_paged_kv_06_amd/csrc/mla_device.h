@@ -108,7 +108,7 @@ struct DecodeParams {
   int32_t* splits;  // written by kernels that schedule in-launch
   uint16_t* out;
   float* lse;
-  float* o_acc;    // [slots][R][512]
+  uint16_t* o_acc;  // [slots][R][512] bf16: normalized split partials
   float* lse_acc;  // [slots][R]   (log2 domain)
   int batch, s_q, h_q, R, max_pages, num_parts, row_groups;
   int causal;
