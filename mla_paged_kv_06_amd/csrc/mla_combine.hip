@@ -54,8 +54,10 @@ __global__ void __launch_bounds__(256) combine_kernel(const uint16_t* __restrict
   }
   // split weights: lanes over splits, a wave max and sum
   const float l0 = t < ns ? lrow[(size_t)t * R] : -INFINITY;
-  float mx = l0;
-  for (int s = t + 64; s < ns; s += 64) mx = fmaxf(mx, lrow[(size_t)s * R]);
+  float l1 = -INFINITY;
+  if (ns > 64 && t + 64 < ns) l1 = lrow[(size_t)(t + 64) * R];  // ns is wave-uniform
+  float mx = fmaxf(l0, l1);
+  for (int s = t + 128; s < ns; s += 64) mx = fmaxf(mx, lrow[(size_t)s * R]);
 #pragma unroll
   for (int d = 32; d >= 1; d >>= 1) mx = fmaxf(mx, __shfl_xor(mx, d));
   uint16_t* orow = out + ((size_t)b * R + row) * kDv + 8 * t;
@@ -65,14 +67,17 @@ __global__ void __launch_bounds__(256) combine_kernel(const uint16_t* __restrict
     return;
   }
   const float e0 = __builtin_amdgcn_exp2f(l0 - mx);  // -inf -> 0
-  float z = e0;
-  for (int s = t + 64; s < ns; s += 64) z += __builtin_amdgcn_exp2f(lrow[(size_t)s * R] - mx);
+  const float e1 = __builtin_amdgcn_exp2f(l1 - mx);
+  float z = e0 + e1;
+  for (int s = t + 128; s < ns; s += 64) z += __builtin_amdgcn_exp2f(lrow[(size_t)s * R] - mx);
 #pragma unroll
   for (int d = 32; d >= 1; d >>= 1) z += __shfl_xor(z, d);
   const float inv = 1.f / z;
-  const float w0 = e0 * inv;  // weight of split t (t < 64)
+  const float w0 = e0 * inv, w1 = e1 * inv;  // weights of splits t and t + 64
   auto weight = [&](int si) __attribute__((always_inline)) {
-    return si < 64 ? lane_value(w0, si) : __builtin_amdgcn_exp2f(lrow[(size_t)si * R] - mx) * inv;
+    return si < 64    ? lane_value(w0, si)
+           : si < 128 ? lane_value(w1, si - 64)
+                      : __builtin_amdgcn_exp2f(lrow[(size_t)si * R] - mx) * inv;
   };
   f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0;
 #pragma unroll
@@ -135,23 +140,22 @@ __global__ void __launch_bounds__(256) combine_wide_kernel(const uint16_t* __res
   const float* lrow = lse_acc + (size_t)s0 * R + row;
   const uint16_t* base = o_acc + ((size_t)s0 * R + row) * kDv + 8 * t;
   // this wave's first kWideUnroll partial rows (splits wv, wv + 4, ...) are
-  // requested first: their loads overlap those of the lse values
+  // requested first: their loads overlap those of the lse values.  Indexes
+  // past the last split read the last one again and are never summed (a
+  // load under a branch made the compiler wait for it on the spot).
   i32x4 v[kWideUnroll];  // raw bf16 partial values, widened where they are summed
 #pragma unroll
   for (int u = 0; u < kWideUnroll; ++u) {
-    const int si = wv + kWaves * u;
-    if (si < ns) {
-      const uint16_t* src = base + (size_t)si * R * kDv;
-      v[u] = *(const i32x4*)src;
-    } else {
-      v[u] = i32x4{0, 0, 0, 0};
-    }
+    const int si = min(wv + kWaves * u, ns - 1);
+    v[u] = *(const i32x4*)(base + (size_t)si * R * kDv);
   }
   // max and sum of the split weights (lanes over splits; every wave computes
   // the same values)
   const float l0 = t < ns ? lrow[(size_t)t * R] : -INFINITY;
-  float mx = l0;
-  for (int s = t + 64; s < ns; s += 64) mx = fmaxf(mx, lrow[(size_t)s * R]);
+  float l1 = -INFINITY;
+  if (ns > 64 && t + 64 < ns) l1 = lrow[(size_t)(t + 64) * R];  // ns is wave-uniform
+  float mx = fmaxf(l0, l1);
+  for (int s = t + 128; s < ns; s += 64) mx = fmaxf(mx, lrow[(size_t)s * R]);
 #pragma unroll
   for (int d = 32; d >= 1; d >>= 1) mx = fmaxf(mx, __shfl_xor(mx, d));
   uint16_t* orow = out + ((size_t)b * R + row) * kDv;
@@ -162,15 +166,18 @@ __global__ void __launch_bounds__(256) combine_wide_kernel(const uint16_t* __res
     }
     return;
   }
-  const float e0 = __builtin_amdgcn_exp2f(l0 - mx);
-  float z = e0;
-  for (int s = t + 64; s < ns; s += 64) z += __builtin_amdgcn_exp2f(lrow[(size_t)s * R] - mx);
+  const float e0 = __builtin_amdgcn_exp2f(l0 - mx);  // -inf -> 0
+  const float e1 = __builtin_amdgcn_exp2f(l1 - mx);
+  float z = e0 + e1;
+  for (int s = t + 128; s < ns; s += 64) z += __builtin_amdgcn_exp2f(lrow[(size_t)s * R] - mx);
 #pragma unroll
   for (int d = 32; d >= 1; d >>= 1) z += __shfl_xor(z, d);
   const float inv = 1.f / z;
-  const float w0 = e0 * inv;  // weight of split t (t < 64)
+  const float w0 = e0 * inv, w1 = e1 * inv;  // weights of splits t and t + 64
   auto weight = [&](int si) __attribute__((always_inline)) {
-    return si < 64 ? lane_value(w0, si) : __builtin_amdgcn_exp2f(lrow[(size_t)si * R] - mx) * inv;
+    return si < 64    ? lane_value(w0, si)
+           : si < 128 ? lane_value(w1, si - 64)
+                      : __builtin_amdgcn_exp2f(lrow[(size_t)si * R] - mx) * inv;
   };
   f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0;
   for (int s = wv; s < ns; s += kWaves * kWideUnroll) {
