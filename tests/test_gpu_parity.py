@@ -255,6 +255,9 @@ def _both_schedules(mla, case, num_cus=0):
     ([700, 0, 2100, 64], 2, 128, 0),           # 4 row groups x 64 partitions
     ([300, 1200], 32, 128, 0),                 # 64 row groups, 4 partitions
     ([900, 65], 3, 40, 1),                     # 120 rows, one partition
+    ([4096] * 16, 1, 16, 0),                   # 16 full rows of a 64-entry block table
+    ([4097] + [4096] * 15, 1, 16, 0),          # one longer row: 65 entries each
+    ([40000, 3000, 9000], 1, 64, 0),           # 64-row kernel, long rows
 ])
 def test_schedule_in_decode_matches_separate(mla, L, s_q, h_q, num_cus):
     """The decode that schedules itself cuts the key range exactly as the
