@@ -399,11 +399,9 @@ __global__ void __launch_bounds__(sv::kThreadsSV, 1)
 #pragma unroll
         for (int k = 0; k < kCopies; ++k) copy_one(cbuf, crs, k);
       }
-      constexpr int DV = 3;
-      bf16x8 vr[DV + 1];
-      static_for<0, DV>([&](auto ic) __attribute__((always_inline)) {
-        load_v(buf, vr[decltype(ic)::value], decltype(ic)::value);
-      });
+      // the rescale decision before the first value fragments are read: the
+      // wait for the factors then covers only them and the weights, which
+      // the copies above have given time to arrive
       if (__builtin_amdgcn_ballot_w64(resc) != 0) {
         static_for<0, kRT>([&](auto rc) __attribute__((always_inline)) {
           constexpr int r2 = decltype(rc)::value;
@@ -412,6 +410,11 @@ __global__ void __launch_bounds__(sv::kThreadsSV, 1)
           });
         });
       }
+      constexpr int DV = 3;
+      bf16x8 vr[DV + 1];
+      static_for<0, DV>([&](auto ic) __attribute__((always_inline)) {
+        load_v(buf, vr[decltype(ic)::value], decltype(ic)::value);
+      });
       static_for<0, kCT>([&](auto ctc) __attribute__((always_inline)) {
         constexpr int ct = decltype(ctc)::value;
         if constexpr (ct + DV < kCT) load_v(buf, vr[(ct + DV) % (DV + 1)], ct + DV);
