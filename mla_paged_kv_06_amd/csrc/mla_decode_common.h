@@ -17,6 +17,16 @@ __device__ __forceinline__ bool item_before(Item a, int eb, int ej) {
 // Wave-uniform value (kept in an SGPR, so loads indexed by it are scalar).
 __device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
+// Wave-uniform read of memory that no kernel of the launch writes (lengths,
+// block table).  Through the constant address space it is always a scalar
+// load, counted by lgkmcnt.  A plain load becomes a vector load wherever the
+// compiler cannot prove the memory unwritten (a kernel that also stores the
+// split counts), and a vector load is counted by vmcnt with the page copies:
+// waiting for it would wait for every copy in flight.
+__device__ __forceinline__ int load_uniform(const int32_t* p, size_t i) {
+  return ((const __attribute__((address_space(4))) int32_t*)p)[i];
+}
+
 // Barrier for LDS traffic only: unlike __syncthreads it does not wait for
 // outstanding global loads, so a page prefetch in flight keeps flying.
 __device__ __forceinline__ void lds_barrier() {

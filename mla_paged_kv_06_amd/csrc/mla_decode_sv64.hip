@@ -185,8 +185,8 @@ __global__ void __launch_bounds__(sv::kThreadsSV, 1)
     }
     n.valid = s.valid && item_before(Item{n.b, n.j}, eb, ej);
     if (n.valid) {
-      if (n.b != s.b) n.L = uni(seqlens[n.b]);
-      if (is_value) n.phys = uni(block_table[(size_t)n.b * prm.max_pages + n.j]);
+      if (n.b != s.b) n.L = load_uniform(seqlens, n.b);
+      if (is_value) n.phys = load_uniform(block_table, (size_t)n.b * prm.max_pages + n.j);
     }
     return n;
   };
@@ -198,8 +198,8 @@ __global__ void __launch_bounds__(sv::kThreadsSV, 1)
     s0.L = L0;
     s0.phys = is_value ? phys0 : 0;
   } else {
-    s0.L = uni(seqlens[b0]);
-    s0.phys = is_value ? uni(block_table[(size_t)b0 * prm.max_pages + j0]) : 0;
+    s0.L = load_uniform(seqlens, b0);
+    s0.phys = is_value ? load_uniform(block_table, (size_t)b0 * prm.max_pages + j0) : 0;
   }
   s0.valid = true;
 
