@@ -215,6 +215,27 @@ def test_many_short_sequences(mla, h_q):
     compare(out, lse, ref_out, ref_lse, batches=pick)
 
 
+@pytest.mark.parametrize("short", [0, 519])
+def test_combine_beyond_128_splits(mla, short):
+    """One 300-page sequence cut at every page (4096 partitions): its rows
+    merge more than 128 partials, so the combine reads split weights from
+    three places (lanes t, t + 64, and memory past 128).  Alone it takes the
+    wide combine; behind 519 one-token sequences (partitions below eight per
+    sequence) the one-wave-per-row combine."""
+    _say(f"[parity] 300-way split behind {short} short sequences")
+    L = [64 * 300 - 5] + [1] * short
+    case = make_case(L, 1, 16, False, seed=61 + short, pool_factor=1.1,
+                     poison_unused=True, poison_tail=True)
+    parts = mla.num_partitions(1, 16, 4096)
+    splits = schedule(L, parts, 1)[1]  # 16 rows: one page unit of fixed cost
+    assert parts == 4096 and splits[1] - splits[0] > 128
+    assert (parts >= 8 * len(L)) == (short == 0)  # which combine runs
+    out, lse = run(mla, case, num_cus=4096)
+    pick = [0, 1, short] if short else [0]
+    ref_out, ref_lse = oracle.decode_ref(case, batches=pick)
+    compare(out, lse, ref_out, ref_lse, batches=pick)
+
+
 @pytest.mark.parametrize("num_cus", [1, 3, 64, 256, 1024, 4096, 5000])
 def test_forced_partition_counts(mla, num_cus):
     _say(f"[parity] num_cus={num_cus}")
