@@ -10,8 +10,9 @@ namespace mla {
 // Combine: merge split partials by log-sum-exp.  One wave per query row
 // (4 rows per workgroup), 8 output columns per lane.  The partial rows of the
 // first kCombineUnroll splits are requested before anything else, so their
-// loads overlap those of the split lse values; the weights of splits below
-// 64 are then broadcast from the lane that computed them.
+// loads overlap those of the split lse values; lane t computes the weights
+// of splits t and t + 64, broadcast from it where they are summed (weights
+// of splits past 128 are computed again from memory).
 constexpr int kCombineRows = 4;
 constexpr int kCombineUnroll = 8;  // partial rows in flight per lane
 
