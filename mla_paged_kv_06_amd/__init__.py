@@ -279,11 +279,11 @@ def schedules_in_decode(batch: int, s_q: int, h_q: int, max_pages: int = 0) -> b
 
 
 def prefers_in_decode(batch: int, s_q: int, h_q: int, max_pages: int = 0) -> bool:
-    """Whether the schedule inside the decode is the faster choice: measured
-    so for at most 16 rows per sequence (one schedule launch saved); with more
-    rows the launch it saves costs less than holding back every workgroup's
-    first copies until the schedule is done."""
-    return s_q * h_q <= 16 and schedules_in_decode(batch, s_q, h_q, max_pages)
+    """Whether the schedule inside the decode is the faster choice: wherever
+    the decode can compute it (one schedule launch saved).  Measured faster
+    or even at 16, 32, 64, 128 and 256 rows per sequence, and even with a
+    single partition."""
+    return schedules_in_decode(batch, s_q, h_q, max_pages)
 
 
 def mla_decode(q, kv_cache, block_table, cache_seqlens, softmax_scale, causal, num_cus: int = 0,

@@ -164,8 +164,8 @@ def test_product_path_does_not_import_the_oracle():
 
 def test_schedule_policy_of_the_binding():
     """Which decodes schedule themselves: capability (at most 1024 sequences,
-    a block table within the 32-bit unit range) and the faster-path choice
-    (at most 16 rows); pure host logic."""
+    a block table within the 32-bit unit range), which the binding also
+    takes as the faster choice; pure host logic."""
     pytest.importorskip("torch")
     import mla_paged_kv_06_amd as m
 
@@ -173,8 +173,10 @@ def test_schedule_policy_of_the_binding():
     assert not m.schedules_in_decode(1025, 1, 16, 64)
     assert not m.schedules_in_decode(1024, 1, 16, 1 << 20)   # 1024 * (2^20 + 2) >= 2^30
     assert m.prefers_in_decode(8, 1, 16, 64)
-    assert not m.prefers_in_decode(8, 2, 16, 64)              # 32 rows: separate launch
-    assert not m.prefers_in_decode(2000, 1, 16, 64)
+    assert m.prefers_in_decode(8, 2, 16, 64)                  # 32 rows
+    assert m.prefers_in_decode(64, 2, 128, 256)               # 256 rows, 4 row groups
+    assert not m.prefers_in_decode(2000, 1, 16, 64)           # more than 1024 sequences
+    assert not m.prefers_in_decode(1024, 1, 16, 1 << 20)      # unit counts past 32 bits
 
 
 def test_fp8_entry_points_reject_bad_arguments(lib):
