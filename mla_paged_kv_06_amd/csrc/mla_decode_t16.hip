@@ -329,26 +329,25 @@ __global__ void __launch_bounds__(kThreads, 1)
         else
           lse_acc[(size_t)slot * prm.R + l16] = lse2;
       }
-      if (direct) {
-        uint16_t* orow = out_ptr + ((size_t)b * prm.R + l16) * kDv + col_base + 4 * g;
-        static_for<0, kCT>([&](auto cc) __attribute__((always_inline)) {
-          constexpr int ct = decltype(cc)::value;
-          const f32x4 v = o[ct] * inv;
-          const bf16x2 a = to_bf16x2(v[0], v[1]);
-          const bf16x2 c = to_bf16x2(v[2], v[3]);
-          *(bf16x4*)(orow + 16 * ct) = bf16x4{a[0], a[1], c[0], c[1]};
-        });
-      } else {
-        // the normalized partial, rounded to bf16 like the output
-        uint16_t* orow = o_acc + ((size_t)slot * prm.R + l16) * kDv + col_base + 4 * g;
-        static_for<0, kCT>([&](auto cc) __attribute__((always_inline)) {
-          constexpr int ct = decltype(cc)::value;
-          const f32x4 v = o[ct] * inv;
-          const bf16x2 a = to_bf16x2(v[0], v[1]);
-          const bf16x2 c = to_bf16x2(v[2], v[3]);
-          *(bf16x4*)(orow + 16 * ct) = bf16x4{a[0], a[1], c[0], c[1]};
-        });
-      }
+      // 16 bytes per lane: lanes g and g ^ 1 (lane ^ 16, the same row) swap
+      // halves so that the even one holds 8 columns of tile c and the odd
+      // one 8 columns of tile c + 1
+      uint16_t* orow = direct ? out_ptr + ((size_t)b * prm.R + l16) * kDv + col_base
+                              : o_acc + ((size_t)slot * prm.R + l16) * kDv + col_base;
+      const bool even = (g & 1) == 0;
+      static_for<0, kCT / 2>([&](auto pc) __attribute__((always_inline)) {
+        constexpr int c = 2 * decltype(pc)::value;
+        const f32x4 va = o[c] * inv;
+        const f32x4 vb = o[c + 1] * inv;
+        const int a0 = __builtin_bit_cast(int, to_bf16x2(va[0], va[1]));
+        const int a1 = __builtin_bit_cast(int, to_bf16x2(va[2], va[3]));
+        const int b0 = __builtin_bit_cast(int, to_bf16x2(vb[0], vb[1]));
+        const int b1 = __builtin_bit_cast(int, to_bf16x2(vb[2], vb[3]));
+        const int r0 = __shfl_xor(even ? b0 : a0, 16);
+        const int r1 = __shfl_xor(even ? b1 : a1, 16);
+        const i32x4 w = even ? i32x4{a0, a1, r0, r1} : i32x4{r0, r1, b0, b1};
+        *(i32x4*)(orow + (even ? 16 * c + 4 * g : 16 * (c + 1) + 4 * (g - 1))) = w;
+      });
     }
     split_idx = 0;  // later sequences of this partition start at their page 0
   };
