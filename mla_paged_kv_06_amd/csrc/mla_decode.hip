@@ -352,6 +352,26 @@ __global__ void __launch_bounds__(kThreads, 1)
     compute_half(tile, j, std::integral_constant<int, 1>{}, cp);
   };
 
+  // one row of this wave's columns, 16 bytes per lane: lanes g and g ^ 1
+  // (lane ^ 16, the same row) swap halves so that the even one holds 8
+  // columns of tile c and the odd one 8 columns of tile c + 1
+  auto store_row = [&](uint16_t* orow, int rt, float inv) __attribute__((always_inline)) {
+    const bool even = (g & 1) == 0;
+    static_for<0, CT / 2>([&](auto pc) __attribute__((always_inline)) {
+      constexpr int c = 2 * decltype(pc)::value;
+      const f32x4 va = o[rt][c] * inv;
+      const f32x4 vb = o[rt][c + 1] * inv;
+      const int a0 = __builtin_bit_cast(int, to_bf16x2(va[0], va[1]));
+      const int a1 = __builtin_bit_cast(int, to_bf16x2(va[2], va[3]));
+      const int b0 = __builtin_bit_cast(int, to_bf16x2(vb[0], vb[1]));
+      const int b1 = __builtin_bit_cast(int, to_bf16x2(vb[2], vb[3]));
+      const int x0 = __shfl_xor(even ? b0 : a0, 16);
+      const int x1 = __shfl_xor(even ? b1 : a1, 16);
+      const i32x4 w = even ? i32x4{a0, a1, x0, x1} : i32x4{x0, x1, b0, b1};
+      *(i32x4*)(orow + (even ? 16 * c + 4 * g : 16 * (c + 1) + 4 * (g - 1))) = w;
+    });
+  };
+
   auto finish_segment = [&](int b) __attribute__((always_inline)) {
     const int s_lo = seg_s_lo;
     const int nsplit = seg_nsplit;
@@ -365,26 +385,11 @@ __global__ void __launch_bounds__(kThreads, 1)
       const float lse2 = lt > 0.f ? m_used[rt] + __builtin_amdgcn_logf(lt) : -INFINITY;
       if (row < prm.R) {
         if (direct) {
-          uint16_t* orow = out_ptr + ((size_t)b * prm.R + row) * kDv + col_base + 4 * g;
-          static_for<0, CT>([&](auto cc) __attribute__((always_inline)) {
-            constexpr int ct = decltype(cc)::value;
-            f32x4 v = o[rt][ct] * inv;
-            bf16x2 a = to_bf16x2(v[0], v[1]);
-            bf16x2 c = to_bf16x2(v[2], v[3]);
-            bf16x4 w = {a[0], a[1], c[0], c[1]};
-            *(bf16x4*)(orow + 16 * ct) = w;
-          });
+          store_row(out_ptr + ((size_t)b * prm.R + row) * kDv + col_base, rt, inv);
           if (g == 0 && wc == 0) lse_ptr[(size_t)b * prm.R + row] = lse2 * kLn2;
         } else {
           // the normalized partial, rounded to bf16 like the output
-          uint16_t* orow = o_acc + ((size_t)slot * prm.R + row) * kDv + col_base + 4 * g;
-          static_for<0, CT>([&](auto cc) __attribute__((always_inline)) {
-            constexpr int ct = decltype(cc)::value;
-            const f32x4 v = o[rt][ct] * inv;
-            const bf16x2 a = to_bf16x2(v[0], v[1]);
-            const bf16x2 c = to_bf16x2(v[2], v[3]);
-            *(bf16x4*)(orow + 16 * ct) = bf16x4{a[0], a[1], c[0], c[1]};
-          });
+          store_row(o_acc + ((size_t)slot * prm.R + row) * kDv + col_base, rt, inv);
           if (g == 0 && wc == 0) lse_acc[(size_t)slot * prm.R + row] = lse2;
         }
       }
