@@ -63,31 +63,36 @@ def algorithmic_work(case):
     return int(nbytes), int(flops)
 
 
-def cpu_baseline(case, budget_s=20.0, min_s=10.0):
-    """Time the oracle (as it stands) on a bounded sample of the workload."""
-    import oracle
-
+def _host_info():
+    """CPU model and the BLAS library numpy calls (name, version, threads)."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    blas = {}
     try:
         from threadpoolctl import threadpool_info
 
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        for i in threadpool_info():
+            if i.get("user_api") == "blas":
+                blas = {"name": i.get("internal_api"), "version": i.get("version"),
+                        "threads": i.get("num_threads"), "arch": i.get("architecture")}
+                break
     except Exception:  # pragma: no cover
-        threads = os.cpu_count() or 1
-    L = case.cache_seqlens.astype(np.int64)
-    order = list(range(case.batch))
-    # estimate per-batch cost by work and take batches until the budget
-    t0 = time.perf_counter()
-    oracle.decode_ref(case, batches=[order[0]])
-    first = time.perf_counter() - t0
-    per_tok = first / max(1, int(L[order[0]]))
-    chosen, est = [], 0.0
-    for b in order:
-        c = per_tok * max(1, int(L[b]))
-        if chosen and est + c > budget_s:
-            break
-        chosen.append(b)
-        est += c
-    # repeat the sample until about min_s of CPU work has been timed
+        pass
+    return model, blas
+
+
+def _time_oracle(case, chosen, min_s):
+    """Seconds per pass of the oracle over the chosen sequences (repeated
+    until about min_s of work has been timed)."""
+    import oracle
+
     reps = 0
     t0 = time.perf_counter()
     while True:
@@ -95,19 +100,65 @@ def cpu_baseline(case, budget_s=20.0, min_s=10.0):
         reps += 1
         if time.perf_counter() - t0 >= min_s:
             break
-    dt = (time.perf_counter() - t0) / reps
-    sub = type(case)(q=case.q[chosen], kv=case.kv, block_table=case.block_table[chosen],
-                     cache_seqlens=case.cache_seqlens[chosen], softmax_scale=case.softmax_scale,
-                     causal=case.causal)
-    nbytes, flops = algorithmic_work(sub)
+    return (time.perf_counter() - t0) / reps, reps
+
+
+def _subcase(case, chosen):
+    return type(case)(q=case.q[chosen], kv=case.kv, block_table=case.block_table[chosen],
+                      cache_seqlens=case.cache_seqlens[chosen], softmax_scale=case.softmax_scale,
+                      causal=case.causal)
+
+
+def cpu_baseline(case, budget_s=20.0, min_s=10.0):
+    """Time the oracle (as it stands) on a bounded sample of the workload,
+    with every BLAS thread the host gives this process; then one thread on
+    the two smallest workloads (tiny, memory-bound) in full."""
+    import oracle
+    from workloads import make_config_case
+
+    model, blas = _host_info()
+    threads = int(blas.get("threads") or len(os.sched_getaffinity(0)))
+    L = case.cache_seqlens.astype(np.int64)
+    order = list(range(case.batch))
+    # estimate per-sequence cost by its tokens and take sequences until the budget
+    t0 = time.perf_counter()
+    oracle.decode_ref(case, batches=[order[0]])
+    per_tok = (time.perf_counter() - t0) / max(1, int(L[order[0]]))
+    chosen, est = [], 0.0
+    for b in order:
+        c = per_tok * max(1, int(L[b]))
+        if chosen and est + c > budget_s:
+            break
+        chosen.append(b)
+        est += c
+    dt, reps = _time_oracle(case, chosen, min_s)
+    nbytes, flops = algorithmic_work(_subcase(case, chosen))
+    single = {}
+    try:
+        from threadpoolctl import threadpool_limits
+
+        with threadpool_limits(limits=1, user_api="blas"):
+            for k in (1, 2):
+                c = make_config_case(k)
+                t1, r1 = _time_oracle(c, list(range(c.batch)), 3.0)
+                nb, fl = algorithmic_work(c)
+                single[WORKLOAD_NAMES[k]] = {"s_per_step": round(t1, 4),
+                                             "GB_per_s": round(nb / t1 / 1e9, 4),
+                                             "GFLOP_per_s": round(fl / t1 / 1e9, 3)}
+    except Exception as e:  # pragma: no cover
+        single = {"skipped": str(e)}
     return {
         "value": round(nbytes / dt / 1e9, 4),
         "unit": "GB/s",
-        "cores": int(threads),
+        "cores": threads,
         "kind": "oracle",
         "sample": f"fp64 numpy oracle over {len(chosen)} of {case.batch} sequences "
                   f"({int(L[chosen].sum())} cached tokens), {reps} timed pass(es) of "
                   f"{dt:.3f} s each; {flops / dt / 1e9:.2f} GFLOP/s",
+        "GFLOP_per_s": round(flops / dt / 1e9, 3),
+        "cpu_model": model,
+        "blas": blas,
+        "single_thread": single,
     }
 
 
@@ -472,53 +523,45 @@ def copy_calibration(mib, launches=5):
     print(json.dumps({"copy_bytes_per_launch": n, "launches": launches}), flush=True)
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5])
-    ap.add_argument("--replicas", type=int, default=0, help="0 = enough to exceed 1 GiB")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-graph", action="store_true")
-    ap.add_argument("--schedule", choices=["auto", "separate", "in_decode"], default="auto",
-                    help="auto: the decode schedules itself where that is faster")
-    ap.add_argument("--no-next-rows", action="store_true",
-                    help="skip timing the absorption products next to the decode")
-    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
-                    help="only run plain device copies of MIB MiB (counter calibration)")
-    args = ap.parse_args()
-
-    world = int(os.environ.get("WORLD_SIZE", "1"))
-    if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU only: the decode path runs on a single MI355X; "
-              "a multi-GPU run is not part of this library", file=sys.stderr)
-        sys.exit(2)
-
+def _capture(fn):
+    """A HIP graph of fn()'s launches on a side stream, replayed once."""
     import torch
 
-    if args.copy_calibration:
-        copy_calibration(args.copy_calibration)
-        return
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        fn()
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    return g
 
-    import mla_paged_kv_06_amd as mla
+
+def _pct(xs):
+    xs = np.asarray(xs, dtype=np.float64)
+    return {"mean": round(float(xs.mean()), 3), "p10": round(float(np.percentile(xs, 10)), 3),
+            "p50": round(float(np.percentile(xs, 50)), 3),
+            "p90": round(float(np.percentile(xs, 90)), 3), "n": int(xs.size)}
+
+
+def measure_workload(mla, k, steps, warmup, dev, replicas=0, schedule="auto", use_graph=True,
+                     per_launch=20):
+    """Time whole steps (schedule + decode + combine) and the decode kernel
+    alone on workload k.  Returns the measurement dict and the case."""
+    import ctypes
+
+    import torch
     from workloads import CONFIGS, make_config_case
 
-    if not torch.cuda.is_available():
-        print("no GPU visible", file=sys.stderr)
-        sys.exit(1)
-    mla.load_library()
-    dev = torch.device("cuda:0")
-    k = args.config
     spec = CONFIGS[k]
     case = make_config_case(k)
     nbytes, flops = algorithmic_work(case)
     print(f"# workload {k} ({spec.name}): batch {case.batch} s_q {case.s_q} h_q {case.h_q} "
           f"sum L {int(case.cache_seqlens.sum())} pool {case.num_pages} pages; "
           f"{nbytes / 1e6:.2f} MB, {flops / 1e9:.2f} GFLOP per step", file=sys.stderr, flush=True)
-
     footprint = case.kv.nbytes + case.q.nbytes + case.block_table.nbytes
-    R = args.replicas or max(2, math.ceil((1 << 30) / footprint))
+    R = replicas or max(2, math.ceil((1 << 30) / footprint))
     q0 = torch.from_numpy(case.q.view(np.int16)).to(dev).view(torch.bfloat16)
     kv0 = torch.from_numpy(case.kv.view(np.int16)).to(dev).view(torch.bfloat16)
     bt0 = torch.from_numpy(case.block_table).to(dev)
@@ -528,78 +571,73 @@ def main():
     b, s_q, h_q = case.batch, case.s_q, case.h_q
     parts = mla.num_partitions(s_q, h_q)
     ws_bytes = mla.workspace_bytes(b, s_q, h_q)
-    bufs = []
-    for _ in range(R):
-        bufs.append(dict(
-            meta=torch.empty((parts, mla.META_INTS), dtype=torch.int32, device=dev),
-            splits=torch.empty((b + 1,), dtype=torch.int32, device=dev),
-            ws=torch.empty((ws_bytes,), dtype=torch.uint8, device=dev),
-            out=torch.empty((b, s_q, h_q, 512), dtype=torch.bfloat16, device=dev),
-            lse=torch.empty((b, s_q, h_q), dtype=torch.float32, device=dev)))
+    bufs = [dict(meta=torch.empty((parts, mla.META_INTS), dtype=torch.int32, device=dev),
+                 splits=torch.empty((b + 1,), dtype=torch.int32, device=dev),
+                 ws=torch.empty((ws_bytes,), dtype=torch.uint8, device=dev),
+                 out=torch.empty((b, s_q, h_q, 512), dtype=torch.bfloat16, device=dev),
+                 lse=torch.empty((b, s_q, h_q), dtype=torch.float32, device=dev))
+            for _ in range(R)]
     lib = mla.load_library()
-    import ctypes
+    vp = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
+    in_decode = schedule == "in_decode" or (
+        schedule == "auto" and mla.prefers_in_decode(b, s_q, h_q, case.max_pages))
 
-    def vp(t):
-        return ctypes.c_void_p(t.data_ptr())
-
-    in_decode = args.schedule == "in_decode" or (
-        args.schedule == "auto" and mla.prefers_in_decode(b, s_q, h_q, case.max_pages))
-
-    def meta_arg(o):
-        return None if in_decode else vp(o["meta"])
-
-    def step(r):
+    def decode(r):
         q, kv, bt, sl = reps[r]
         o = bufs[r]
         st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
-        s1 = 0
-        if not in_decode:
-            s1 = lib.mla_get_metadata(vp(sl), b, s_q, h_q, 0, vp(o["meta"]), vp(o["splits"]), st)
         s2 = lib.mla_decode_paged(vp(q), vp(kv), vp(bt), vp(sl), b, s_q, h_q, case.num_pages,
                                   case.max_pages, case.softmax_scale, int(case.causal),
-                                  meta_arg(o), vp(o["splits"]), 0, vp(o["ws"]), ws_bytes,
-                                  vp(o["out"]), vp(o["lse"]), st)
+                                  None if in_decode else vp(o["meta"]), vp(o["splits"]), 0,
+                                  vp(o["ws"]), ws_bytes, vp(o["out"]), vp(o["lse"]), st)
+        if s2:
+            raise RuntimeError(f"decode status {s2}")
+
+    def step(r):
+        sl = reps[r][3]
+        o = bufs[r]
+        st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        if not in_decode:
+            s1 = lib.mla_get_metadata(vp(sl), b, s_q, h_q, 0, vp(o["meta"]), vp(o["splits"]), st)
+            if s1:
+                raise RuntimeError(f"metadata status {s1}")
+        decode(r)
         s3 = lib.mla_combine(vp(o["ws"]), ws_bytes, vp(o["splits"]), b, s_q, h_q, 0,
                              vp(o["out"]), vp(o["lse"]), st)
-        if s1 or s2 or s3:
-            raise RuntimeError(f"library status {s1} {s2} {s3}")
+        if s3:
+            raise RuntimeError(f"combine status {s3}")
 
     # eager warmup (also sanity: every replica once)
-    for i in range(max(args.warmup, R)):
+    for i in range(max(warmup, R)):
         step(i % R)
     torch.cuda.synchronize()
 
-    K = args.steps
+    # graphs of G = min(K, R) steps (each on its own replica) and of the
+    # remainder, so that the timed region is K steps replayed from graphs
+    K = steps
+    G = min(K, R)
+    full, rem = divmod(K, G)
     timing = "hip-graph"
-
-    def capture(fn):
-        s = torch.cuda.Stream()
-        s.wait_stream(torch.cuda.current_stream())
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g, stream=s):
-            fn()
-        torch.cuda.synchronize()
-        g.replay()
-        torch.cuda.synchronize()
-        return g
-
-    graph = None
-    if not args.no_graph:
+    graph = rgraph = None
+    if use_graph:
         try:
-            graph = capture(lambda: [step(r) for r in range(R)])
-        except Exception as e:  # capture not available: fall back to eager launches
+            graph = _capture(lambda: [step(r) for r in range(G)])
+            if rem:
+                rgraph = _capture(lambda: [step(r) for r in range(rem)])
+        except Exception as e:  # capture not available: eager launches
             print(f"# graph capture failed ({e}); timing eager launches", file=sys.stderr)
-            graph, timing = None, "eager"
+            graph = rgraph = None
+    if graph is None:
+        timing = "eager"
 
-    # ---- timed region: exactly K whole steps (schedule + decode + combine)
+    # ---- timed region: exactly K whole steps
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     if graph is not None:
-        full, rem = divmod(K, R)
         for _ in range(full):
             graph.replay()
-        for r in range(rem):
-            step(r)
+        if rgraph is not None:
+            rgraph.replay()
     else:
         for i in range(K):
             step(i % R)
@@ -607,40 +645,39 @@ def main():
     elapsed = time.perf_counter() - t0
     ms_per_step = elapsed * 1e3 / K
 
-    # ---- decode kernel duration: HIP events on the launch stream around
-    # back-to-back decode launches (one per replica, schedules already built)
-    def decodes():
-        for r in range(R):
-            q, kv, bt, sl = reps[r]
-            o = bufs[r]
-            st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
-            st2 = lib.mla_decode_paged(vp(q), vp(kv), vp(bt), vp(sl), b, s_q, h_q, case.num_pages,
-                                       case.max_pages, case.softmax_scale, int(case.causal),
-                                       meta_arg(o), vp(o["splits"]), 0, vp(o["ws"]), ws_bytes,
-                                       vp(o["out"]), vp(o["lse"]), st)
-            if st2:
-                raise RuntimeError(f"decode status {st2}")
-
+    # ---- decode kernel: HIP events on the launch stream around a graph of
+    # back-to-back decode launches (one per replica, schedules built above)
     dgraph = None
     if graph is not None:
         try:
-            dgraph = capture(decodes)
+            dgraph = _capture(lambda: [decode(r) for r in range(R)])
         except Exception as e:
             print(f"# decode graph capture failed ({e})", file=sys.stderr)
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
-    n_rep = max(3, K // R)
+    n_rep = max(5, K // R)
     dec_ms = []
     for _ in range(n_rep):
         e0.record()
         if dgraph is not None:
             dgraph.replay()
         else:
-            decodes()
+            for r in range(R):
+                decode(r)
         e1.record()
         torch.cuda.synchronize()
         dec_ms.append(e0.elapsed_time(e1) / R)
     dec_avg_ms = float(np.mean(dec_ms))
+    # ---- spread: each launch alone between two events (eager; the markers
+    # add about a microsecond, which matters only for the smallest workloads)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(per_launch)]
+    for i, (a, z) in enumerate(evs):
+        a.record()
+        decode(i % R)
+        z.record()
+    torch.cuda.synchronize()
+    each_us = [a.elapsed_time(z) * 1e3 for a, z in evs]
 
     value = nbytes / (ms_per_step * 1e-3) / 1e9
     achieved = nbytes / (dec_avg_ms * 1e-3) / 1e9
@@ -655,49 +692,237 @@ def main():
         roofline = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4)}
     roofline["traffic"] = measured_traffic(WORKLOAD_NAMES[k])
+    m = {
+        "workload": WORKLOAD_NAMES[k], "config_index": k,
+        "batch": b, "s_q": s_q, "h_q": h_q, "causal": bool(case.causal),
+        "cache_seqlens": list(spec.lengths), "sum_seqlen": int(case.cache_seqlens.sum()),
+        "seed": 1000 + k, "replicas": R, "timing": timing,
+        "graph_steps": G if graph is not None else 0,
+        "graph_replays": (full + (1 if rgraph is not None else 0)) if graph is not None else 0,
+        "schedule": "in-decode" if in_decode else "separate-launch",
+        "value_GB_per_s": round(value, 2), "ms_per_step": round(ms_per_step, 5),
+        "step_tflops": round(flops / (ms_per_step * 1e-3) / 1e12, 3),
+        "algorithmic": {"bytes_per_step": int(nbytes), "flops_per_step": int(flops)},
+        "decode_kernel_ms": round(dec_avg_ms, 5),
+        "decode_us_graph": _pct([x * 1e3 for x in dec_ms]),
+        "decode_us_per_launch": _pct(each_us),
+        "decode_launches_timed": n_rep * R,
+        "decode_GB_per_s": round(achieved, 1), "decode_tflops": round(dec_tflops, 3),
+        "hbm_frac": round(achieved / HBM_PEAK_GBS, 4),
+        "mfma_frac": round(dec_tflops / BF16_PEAK_TFLOPS, 4),
+        "roofline": roofline,
+    }
+    del reps, bufs
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return m, case
+
+
+def machine_limits(mla, dev):
+    """What this GPU reaches on plain work: a streaming read of 2 GiB (HBM)
+    and a loop of bf16 16x16x32 matrix instructions (matrix cores), with the
+    shader clock sampled under matrix load."""
+    import ctypes
+
+    import torch
+
+    lib = mla.load_library()
+    st = lambda: ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)  # noqa: E731
+    nbytes = 2 << 30
+    buf = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(3)
+    blocks = 2048
+    sink = torch.empty(max(blocks, 256 * 4), dtype=torch.int32, device=dev)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    ts = []
+    for it in range(6):
+        e0.record()
+        rc = lib.mla_probe_stream_read(ctypes.c_void_p(buf.data_ptr()), nbytes,
+                                       ctypes.c_void_p(sink.data_ptr()), blocks, st())
+        e1.record()
+        torch.cuda.synchronize()
+        if rc:
+            raise RuntimeError(f"probe status {rc}")
+        if it:
+            ts.append(e0.elapsed_time(e1))
+    read_gbs = nbytes / (float(np.median(ts)) * 1e-3) / 1e9
+    del buf
+    # matrix loop: 256 workgroups of 8 waves, 4 chains each
+    mblocks, iters = 256, 20000
+    msink = torch.empty(mblocks * 512, dtype=torch.float32, device=dev)
+    clk = torch.zeros(2, dtype=torch.int64, device=dev)
+    ts, ghz = [], []
+    for it in range(4):
+        e0.record()
+        rc = lib.mla_probe_mfma(iters, mblocks, ctypes.c_void_p(msink.data_ptr()),
+                                ctypes.c_void_p(clk.data_ptr()), st())
+        e1.record()
+        torch.cuda.synchronize()
+        if rc:
+            raise RuntimeError(f"probe status {rc}")
+        if it:
+            ts.append(e0.elapsed_time(e1))
+            c = clk.cpu().numpy()
+            ghz.append(float(c[0]) / (float(c[1]) / 100e6) / 1e9)
+    mflops = mblocks * 8 * iters * 4 * 16384
+    mfma_tf = mflops / (float(np.median(ts)) * 1e-3) / 1e12
+    torch.cuda.empty_cache()
+    return {"stream_read_GB_per_s": round(read_gbs, 1),
+            "stream_read_frac_of_spec": round(read_gbs / HBM_PEAK_GBS, 4),
+            "stream_read_bytes": nbytes,
+            "mfma_loop_TFLOP_per_s": round(mfma_tf, 1),
+            "mfma_loop_frac_of_spec": round(mfma_tf / BF16_PEAK_TFLOPS, 4),
+            "shader_clock_GHz_under_mfma": round(float(np.median(ghz)), 3),
+            "spec_clock_GHz": 2.4}
+
+
+def trace_stats(path):
+    """Per-kernel dispatch durations (count, mean, p10, p50, p90 in us) from a
+    rocprofv3 kernel-trace CSV."""
+    import csv
+
+    dur = {}
+    with open(path) as fh:
+        for row in csv.DictReader(fh):
+            name = row.get("Kernel_Name") or row.get("KernelName") or "?"
+            t = int(row["End_Timestamp"]) - int(row["Start_Timestamp"])
+            dur.setdefault(name, []).append(t / 1e3)
+    out = {}
+    for name, xs in sorted(dur.items(), key=lambda kv: -sum(kv[1])):
+        out[name] = _pct(xs)
+    print(json.dumps(out, indent=1))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=4, choices=[1, 2, 3, 4, 5],
+                    help="headline workload (default 4, the largest)")
+    ap.add_argument("--others", default="2,3,5",
+                    help="workloads measured beside the headline ('' for none)")
+    ap.add_argument("--replicas", type=int, default=0, help="0 = enough to exceed 1 GiB")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--no-probes", action="store_true",
+                    help="skip the streaming-read and matrix-loop machine limits")
+    ap.add_argument("--schedule", choices=["auto", "separate", "in_decode"], default="auto",
+                    help="auto: the decode schedules itself where that is faster")
+    ap.add_argument("--no-next-rows", action="store_true",
+                    help="skip timing the rows next to the decode")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run plain device copies of MIB MiB (counter calibration)")
+    ap.add_argument("--probes-only", action="store_true",
+                    help="only run the machine-limit probes and print them")
+    ap.add_argument("--trace-stats", default="", metavar="CSV",
+                    help="only summarise a rocprofv3 kernel-trace CSV (no GPU)")
+    args = ap.parse_args()
+
+    if args.trace_stats:
+        trace_stats(args.trace_stats)
+        return
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: the decode path runs on a single MI355X; "
+              "a multi-GPU run is not part of this library", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
+
+    import mla_paged_kv_06_amd as mla
+    from workloads import make_config_case
+
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    mla.load_library()
+    dev = torch.device("cuda:0")
+    if args.probes_only:
+        print(json.dumps(machine_limits(mla, dev)), flush=True)
+        return
+
+    k = args.config
+    head, case = measure_workload(mla, k, args.steps, args.warmup, dev, args.replicas,
+                                  args.schedule, not args.no_graph)
+    limits = None if args.no_probes else machine_limits(mla, dev)
+    roofline = dict(head["roofline"])
+    if limits:
+        if roofline["bound"] == "mfma":
+            roofline["frac_of_measured_peak"] = round(
+                roofline["achieved"] / limits["mfma_loop_TFLOP_per_s"], 4)
+        else:
+            roofline["frac_of_measured_peak"] = round(
+                roofline["achieved"] / limits["stream_read_GB_per_s"], 4)
     res = {
         "metric": METRIC,
-        "value": round(value, 2),
+        "value": head["value_GB_per_s"],
         "unit": "GB/s",
         "n_gpus": 1,
-        "steps": K,
+        "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 5),
+        "ms_per_step": head["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
         "config": {
-            "workload": WORKLOAD_NAMES[k],
-            "batch": b, "s_q": s_q, "h_q": h_q, "head_dim": 576, "v_dim": 512, "page": 64,
-            "cache_seqlens": list(spec.lengths), "sum_seqlen": int(case.cache_seqlens.sum()),
-            "causal": bool(case.causal), "seed": 1000 + k, "replicas": R,
-            "timing": timing, "decode_launches_timed": n_rep * R,
-            "schedule": "in-decode" if in_decode else "separate-launch",
+            "workload": head["workload"],
+            "batch": head["batch"], "s_q": head["s_q"], "h_q": head["h_q"], "head_dim": 576,
+            "v_dim": 512, "page": 64, "cache_seqlens": head["cache_seqlens"],
+            "sum_seqlen": head["sum_seqlen"], "causal": head["causal"], "seed": head["seed"],
+            "replicas": head["replicas"], "timing": head["timing"],
+            "graph_steps": head["graph_steps"], "graph_replays": head["graph_replays"],
+            "decode_launches_timed": head["decode_launches_timed"],
+            "schedule": head["schedule"],
         },
-        "algorithmic": {"bytes_per_step": int(nbytes), "flops_per_step": int(flops)},
-        "tflops": round(flops / (ms_per_step * 1e-3) / 1e12, 3),
-        "decode_kernel_ms": round(dec_avg_ms, 5),
-        "decode_tflops": round(flops / (dec_avg_ms * 1e-3) / 1e12, 3),
+        "algorithmic": head["algorithmic"],
+        "tflops": head["step_tflops"],
+        "decode_kernel_ms": head["decode_kernel_ms"],
+        "decode_us_graph": head["decode_us_graph"],
+        "decode_us_per_launch": head["decode_us_per_launch"],
+        "decode_tflops": head["decode_tflops"],
         "roofline": roofline,
-        "hbm_frac": round(achieved / HBM_PEAK_GBS, 4),
-        "mfma_frac": round(dec_tflops / BF16_PEAK_TFLOPS, 4),
+        "hbm_frac": head["hbm_frac"],
+        "mfma_frac": head["mfma_frac"],
     }
+    if limits:
+        res["machine_limits"] = limits
+    others = [int(x) for x in args.others.split(",") if x.strip()] if args.others else []
+    res["workloads"] = {}
+    for k2 in others:
+        if k2 == k:
+            continue
+        m2, _ = measure_workload(mla, k2, args.steps, args.warmup, dev, 0, args.schedule,
+                                 not args.no_graph)
+        if limits:
+            r2 = m2["roofline"]
+            ref = limits["mfma_loop_TFLOP_per_s"] if r2["bound"] == "mfma" else \
+                limits["stream_read_GB_per_s"]
+            r2["frac_of_measured_peak"] = round(r2["achieved"] / ref, 4)
+        res["workloads"][m2["workload"]] = m2
     if not args.no_next_rows:
+        b, s_q, h_q = case.batch, case.s_q, case.h_q
+        c2 = make_config_case(2)
         res["next_rows"] = {
             "absorption": absorption_rates(mla, b, s_q, h_q, 2000 + k, dev),
-            "kv_append": kv_append_rates(mla, [int(x) for x in case.cache_seqlens], s_q, 3000 + k,
-                                         dev),
+            "kv_append": kv_append_rates(mla, [int(x) for x in case.cache_seqlens], s_q,
+                                         3000 + k, dev),
+            # the FP8 cache decode takes at most 16 rows: the memory-bound workload
+            "fp8_cache": fp8_cache_rates(mla, c2, dev),
             # more query tokens per sequence: 2 and 4 speculative tokens on
             # the memory-bound workload's sequences (32 and 64 rows), and a
             # 512-token chunk at 128 heads over a 4096-token cache
-            "fp8_cache": fp8_cache_rates(mla, case, dev),
             "query_tokens": {
                 "speculative_s_q2": query_token_rates(
-                    mla, [int(x) for x in make_config_case(2).cache_seqlens], 2, 16, 4001, dev),
+                    mla, [int(x) for x in c2.cache_seqlens], 2, 16, 4001, dev),
                 "speculative_s_q4": query_token_rates(
-                    mla, [int(x) for x in make_config_case(2).cache_seqlens], 4, 16, 4002, dev),
+                    mla, [int(x) for x in c2.cache_seqlens], 4, 16, 4002, dev),
                 "chunk_512x128": query_token_rates(mla, [4096], 512, 128, 4003, dev),
             },
         }

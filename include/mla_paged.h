@@ -50,9 +50,13 @@
  *
  * Errors.  Host-visible arguments are checked before anything is launched; a
  * failed check returns a status and launches nothing.  A failed launch
- * returns MLA_ERR_HIP.  Device-side contents are preconditions that are not
- * checked: every cache_seqlens[b] in [0, max_pages*64], and every used
- * block_table entry in [0, num_pages).  No C++ exception crosses this ABI.
+ * returns MLA_ERR_HIP.  Device-side contents are preconditions: every
+ * cache_seqlens[b] in [0, max_pages*64], and every used block_table entry
+ * (j < ceil(L_b/64)) in [0, num_pages).  They are not checked unless debug
+ * checks are on (MLA_DEBUG=1 in the environment, or mla_set_debug_checks):
+ * then each decode call first checks them on the device, waits for the
+ * result, and returns MLA_ERR_DEVICE_CONTENTS without launching the decode
+ * if any is violated.  No C++ exception crosses this ABI.
  */
 #ifndef MLA_PAGED_H
 #define MLA_PAGED_H
@@ -71,7 +75,8 @@ typedef enum {
   MLA_ERR_INVALID_ARGUMENT = 1, /* null pointer, non-positive size, bad scale */
   MLA_ERR_UNSUPPORTED = 2,      /* shape outside the supported limits below */
   MLA_ERR_WORKSPACE_TOO_SMALL = 3,
-  MLA_ERR_HIP = 4               /* a HIP runtime call or launch failed */
+  MLA_ERR_HIP = 4,              /* a HIP runtime call or launch failed */
+  MLA_ERR_DEVICE_CONTENTS = 5   /* debug checks: a length or used block-table entry out of range */
 } mla_status_t;
 
 #define MLA_HEAD_DIM 576
@@ -86,6 +91,20 @@ typedef enum {
 #define MLA_MAX_APPEND 65536 /* new tokens per sequence in one mla_kv_append */
 #define MLA_MAX_FUSED_BATCH 1024 /* sequences for a decode that schedules itself */
 #define MLA_FP8_TOKEN_BYTES 656  /* one token of the FP8 latent cache (see mla_kv_quantize_fp8) */
+
+/*
+ * Debug checks of device contents before every mla_decode_paged /
+ * mla_decode_paged_fp8 call (see "Errors" above).  on = 1 turns them on,
+ * 0 off, a negative value leaves the setting as it is; returns the previous
+ * setting (1 or 0).  The first call of the library takes the default from
+ * the environment: on when MLA_DEBUG is set to anything but "0".  With the
+ * checks on, a decode waits for its stream (one small check launch and a
+ * 4-byte read back) and returns MLA_ERR_UNSUPPORTED on a stream under graph
+ * capture.  The checks read only the lengths and the block-table entries
+ * the decode would read; their error word is a 4-byte device variable per
+ * GPU, shared by every call on it.
+ */
+int32_t mla_set_debug_checks(int32_t on);
 
 /*
  * Number of key-range partitions used for `num_cus` compute units
@@ -140,7 +159,8 @@ mla_status_t mla_get_metadata(const int32_t* cache_seqlens, int32_t batch, int32
  * and writes num_splits (batch + 1 ints, device) for mla_combine; larger
  * batches or block tables with a NULL tile_metadata return
  * MLA_ERR_UNSUPPORTED.  With tile_metadata given, num_splits is only read.
- * softmax_scale must be finite and positive (the pages' 1/sqrt(d) scaling);
+ * softmax_scale must be finite and positive (the workloads use 1/sqrt(192),
+ * the per-head query width before absorption; the pages state no scale);
  * anything else returns MLA_ERR_INVALID_ARGUMENT.
  */
 mla_status_t mla_decode_paged(const void* q, const void* kv_cache, const int32_t* block_table,
@@ -272,6 +292,25 @@ mla_status_t mla_decode_paged_fp8(const void* q, const void* kv_fp8, const int32
                                   const int32_t* tile_metadata, int32_t* num_splits,
                                   int32_t num_cus, void* workspace, size_t workspace_bytes,
                                   void* out, float* lse, hipStream_t stream);
+
+/*
+ * Machine-limit probes (benchmark instruments, not part of the decode).
+ * mla_probe_stream_read reads `bytes` (a multiple of 16, >= 16) of device
+ * memory at `buf` (16-byte aligned) once with 16-byte loads from `blocks`
+ * workgroups of 256 threads and writes one 4-byte word per workgroup to
+ * `sink` (device, blocks * 4 bytes): its duration gives the streaming-read
+ * rate this GPU reaches.  mla_probe_mfma runs `iters` x 4 independent bf16
+ * 16x16x32 matrix instructions in each of 8 waves of `blocks` workgroups
+ * (16384 flops each), no memory traffic; it writes blocks * 512 floats to
+ * `sink` and, from workgroup 0, two 8-byte counts to `clocks` (device): the
+ * shader-clock cycles and the 100 MHz real-time ticks its loop took, whose
+ * ratio is the shader clock under matrix load.  Asynchronous on `stream`;
+ * MLA_ERR_INVALID_ARGUMENT for null pointers or sizes out of range.
+ */
+mla_status_t mla_probe_stream_read(const void* buf, size_t bytes, void* sink, int32_t blocks,
+                                   hipStream_t stream);
+mla_status_t mla_probe_mfma(int32_t iters, int32_t blocks, void* sink, void* clocks,
+                            hipStream_t stream);
 
 /* Static, human-readable text of a status code. */
 const char* mla_status_string(mla_status_t status);

@@ -40,6 +40,7 @@ __all__ = [
     "decode_paged_fp8",
     "mla_decode_fp8",
     "FP8_TOKEN_BYTES",
+    "set_debug_checks",
 ]
 
 HEAD_DIM = 576
@@ -103,6 +104,12 @@ def load_library() -> ctypes.CDLL:
     lib.mla_kv_quantize_fp8.restype = ctypes.c_int
     lib.mla_decode_paged_fp8.argtypes = list(lib.mla_decode_paged.argtypes)
     lib.mla_decode_paged_fp8.restype = ctypes.c_int
+    lib.mla_probe_stream_read.argtypes = [vp, sz, vp, i32, vp]
+    lib.mla_probe_stream_read.restype = ctypes.c_int
+    lib.mla_probe_mfma.argtypes = [i32, i32, vp, vp, vp]
+    lib.mla_probe_mfma.restype = ctypes.c_int
+    lib.mla_set_debug_checks.argtypes = [i32]
+    lib.mla_set_debug_checks.restype = i32
     lib.mla_status_string.argtypes = [ctypes.c_int]
     lib.mla_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -135,6 +142,13 @@ def _need(t: torch.Tensor, name: str, dtype: torch.dtype, dims: int) -> None:
         raise ValueError(f"{name} must have {dims} dims, got shape {tuple(t.shape)}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
+
+
+def set_debug_checks(on: Optional[bool] = None) -> bool:
+    """Turn the device-content checks before every decode on or off (None
+    leaves them as they are); returns the previous setting.  The default
+    comes from MLA_DEBUG in the environment."""
+    return bool(load_library().mla_set_debug_checks(-1 if on is None else int(bool(on))))
 
 
 def num_partitions(s_q: int, h_q: int, num_cus: int = 0) -> int:

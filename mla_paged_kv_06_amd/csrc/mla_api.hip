@@ -7,10 +7,20 @@
 #include <cmath>
 #include <cstddef>
 #include <cstdint>
+#include <cstdlib>
+#include <cstring>
 
 #include "mla_paged.h"
 #include "mla_device.h"
 
+extern "C" hipError_t mla_check_word_address(int** addr);
+extern "C" hipError_t mla_launch_check_contents(const int32_t* seqlens, const int32_t* block_table,
+                                                int batch, int max_pages, int num_pages, int* word,
+                                                hipStream_t stream);
+extern "C" hipError_t mla_launch_probe_stream_read(const void* src, size_t bytes, unsigned* sink,
+                                                   int blocks, hipStream_t stream);
+extern "C" hipError_t mla_launch_probe_mfma(int iters, int blocks, float* sink,
+                                            unsigned long long* clk, hipStream_t stream);
 extern "C" hipError_t mla_launch_sched(const int32_t* seqlens, int batch, int num_parts, int c0,
                                        int32_t* meta, int32_t* splits, hipStream_t stream);
 
@@ -35,6 +45,53 @@ bool rows_ok(int32_t s_q, int32_t h_q) {
   if (s_q <= 0 || h_q <= 0) return false;
   const long long R = (long long)s_q * h_q;
   return R <= MLA_MAX_ROWS;
+}
+
+// Debug checks of device contents: -1 = not decided yet (then MLA_DEBUG in
+// the environment decides), 0 = off, 1 = on.
+std::atomic<int> g_debug{-1};
+
+bool debug_checks_on() {
+  int v = g_debug.load(std::memory_order_relaxed);
+  if (v < 0) {
+    const char* e = std::getenv("MLA_DEBUG");
+    v = (e && *e && std::strcmp(e, "0") != 0) ? 1 : 0;
+    int expect = -1;
+    g_debug.compare_exchange_strong(expect, v, std::memory_order_relaxed);
+  }
+  return v > 0;
+}
+
+// Address of the current device's check word, looked up once per device.
+std::atomic<int*> g_check_word[kMaxDevices];
+
+int* check_word() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  int* p = g_check_word[dev].load(std::memory_order_acquire);
+  if (p) return p;
+  if (mla_check_word_address(&p) != hipSuccess) return nullptr;
+  g_check_word[dev].store(p, std::memory_order_release);
+  return p;
+}
+
+// Runs the content checks on `stream` and waits for them.  MLA_OK when the
+// lengths and the used block-table entries are in range.
+mla_status_t check_device_contents(const int32_t* seqlens, const int32_t* block_table,
+                                   int batch, int max_pages, int num_pages, hipStream_t stream) {
+  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(stream, &cap) != hipSuccess) return MLA_ERR_HIP;
+  if (cap != hipStreamCaptureStatusNone) return MLA_ERR_UNSUPPORTED;  // it must wait
+  int* word = check_word();
+  if (!word) return MLA_ERR_HIP;
+  if (mla_launch_check_contents(seqlens, block_table, batch, max_pages, num_pages, word,
+                                stream) != hipSuccess)
+    return MLA_ERR_HIP;
+  int flags = 0;
+  if (hipMemcpyAsync(&flags, word, sizeof(int), hipMemcpyDeviceToHost, stream) != hipSuccess)
+    return MLA_ERR_HIP;
+  if (hipStreamSynchronize(stream) != hipSuccess) return MLA_ERR_HIP;
+  return flags ? MLA_ERR_DEVICE_CONTENTS : MLA_OK;
 }
 
 int row_groups_of(int R) { return (R + mla::kRowGroup - 1) / mla::kRowGroup; }
@@ -104,6 +161,12 @@ extern "C" hipError_t mla_launch_kv_append(uint16_t* kv, int32_t* block_table, i
 
 extern "C" {
 
+int32_t mla_set_debug_checks(int32_t on) {
+  const int prev = debug_checks_on() ? 1 : 0;
+  if (on >= 0) g_debug.store(on ? 1 : 0, std::memory_order_relaxed);
+  return prev;
+}
+
 int32_t mla_num_partitions(int32_t s_q, int32_t h_q, int32_t num_cus) {
   return parts_of(s_q, h_q, num_cus);
 }
@@ -161,6 +224,12 @@ static mla_status_t decode_impl(bool fp8, const void* q, const void* kv_cache, c
   if (!tile_metadata && (batch > MLA_MAX_FUSED_BATCH ||
                          (long long)batch * ((long long)max_pages + 2) >= (1LL << 30)))
     return MLA_ERR_UNSUPPORTED;
+
+  if (debug_checks_on()) {
+    const mla_status_t st =
+        check_device_contents(cache_seqlens, block_table, batch, max_pages, num_pages, stream);
+    if (st != MLA_OK) return st;
+  }
 
   mla::DecodeParams prm;
   prm.q = (const uint16_t*)q;
@@ -296,6 +365,24 @@ mla_status_t mla_kv_append(void* kv_cache, int32_t num_pages, int32_t* block_tab
   return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 
+mla_status_t mla_probe_stream_read(const void* buf, size_t bytes, void* sink, int32_t blocks,
+                                   hipStream_t stream) {
+  if (!buf || !sink || blocks <= 0 || bytes < 16 || (bytes & 15) || ((uintptr_t)buf & 15))
+    return MLA_ERR_INVALID_ARGUMENT;
+  return mla_launch_probe_stream_read(buf, bytes, (unsigned*)sink, blocks, stream) == hipSuccess
+             ? MLA_OK
+             : MLA_ERR_HIP;
+}
+
+mla_status_t mla_probe_mfma(int32_t iters, int32_t blocks, void* sink, void* clocks,
+                            hipStream_t stream) {
+  if (!sink || !clocks || iters <= 0 || blocks <= 0) return MLA_ERR_INVALID_ARGUMENT;
+  return mla_launch_probe_mfma(iters, blocks, (float*)sink, (unsigned long long*)clocks, stream) ==
+                 hipSuccess
+             ? MLA_OK
+             : MLA_ERR_HIP;
+}
+
 const char* mla_status_string(mla_status_t status) {
   switch (status) {
     case MLA_OK: return "ok";
@@ -303,6 +390,8 @@ const char* mla_status_string(mla_status_t status) {
     case MLA_ERR_UNSUPPORTED: return "unsupported shape";
     case MLA_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
     case MLA_ERR_HIP: return "HIP runtime error";
+    case MLA_ERR_DEVICE_CONTENTS:
+      return "cache length or block-table entry out of range (debug checks)";
   }
   return "unknown status";
 }

@@ -1,7 +1,10 @@
-// LSE combine of split partials (FlashMLA release note, paragraph on
-// variable-length sequences: a long sequence is split over several compute
-// units, each producing a partial result whose log-sum-exp lets the partials
-// be merged exactly).
+// LSE combine of split partials.  Splitting one sequence's keys over several
+// compute units and merging the partial results is this library's design for
+// balancing variable-length sequences (the FlashMLA release note says only
+// that its kernel is tuned for variable-length sequences; the get-metadata /
+// decode / combine call split follows the problem statement).  The merge is
+// exact: with s_k the scores of split k, lse = ln sum_k exp(lse_k) and
+// out = sum_k exp(lse_k - lse) o_k reproduce the unsplit softmax.
 
 #include "mla_device.h"
 

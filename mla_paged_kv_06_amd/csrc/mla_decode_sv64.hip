@@ -186,7 +186,12 @@ __global__ void __launch_bounds__(sv::kThreadsSV, 1)
     n.valid = s.valid && item_before(Item{n.b, n.j}, eb, ej);
     if (n.valid) {
       if (n.b != s.b) n.L = load_uniform(seqlens, n.b);
-      if (is_value) n.phys = load_uniform(block_table, (size_t)n.b * prm.max_pages + n.j);
+      // only pages that hold tokens have a block-table entry (an empty
+      // sequence's single unit holds none); the others get page 0 and a
+      // resource of zero bytes
+      if (is_value)
+        n.phys = n.j * kPage < n.L ? load_uniform(block_table, (size_t)n.b * prm.max_pages + n.j)
+                                   : 0;
     }
     return n;
   };
@@ -199,7 +204,9 @@ __global__ void __launch_bounds__(sv::kThreadsSV, 1)
     s0.phys = is_value ? phys0 : 0;
   } else {
     s0.L = load_uniform(seqlens, b0);
-    s0.phys = is_value ? load_uniform(block_table, (size_t)b0 * prm.max_pages + j0) : 0;
+    s0.phys = (is_value && j0 * kPage < s0.L)
+                  ? load_uniform(block_table, (size_t)b0 * prm.max_pages + j0)
+                  : 0;
   }
   s0.valid = true;
 

@@ -78,9 +78,10 @@ __global__ void __launch_bounds__(kThreads, 1)
   const int l16 = lane & 15;
   const int g = lane >> 4;
 
-  // XCD-aware mapping: consecutive partitions go to different XCDs
-  const int bid = blockIdx.x;
-  const int part = (bid >> 3) * 8 + (bid & 7);
+  // one partition per workgroup: partitions read disjoint pages (no L2
+  // reuse between workgroups), so their placement over the XCDs is left to
+  // the dispatcher's round robin
+  const int part = blockIdx.x;
   if (part >= prm.num_parts) return;
 
   int eb, ej, split_idx;

@@ -1,0 +1,106 @@
+// Machine-limit probes used by the benchmark to put the decode's rates next
+// to what this chip reaches on plain work of each kind:
+//   - a streaming read of a large buffer (the HBM ceiling a kernel that only
+//     reads can reach), 16-byte loads, several in flight per lane;
+//   - a loop of independent bf16 matrix instructions, 16x16x32, with no
+//     memory traffic at all (the matrix-core ceiling), which also samples
+//     the shader clock against the constant 100 MHz real-time counter.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mla {
+
+typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
+typedef __attribute__((ext_vector_type(8))) __bf16 pbf16x8;
+typedef __attribute__((ext_vector_type(4))) float pf32x4;
+
+constexpr int kStreamThreads = 256;
+constexpr int kStreamUnroll = 8;  // 16-byte loads in flight per lane
+
+// Every lane reads kStreamUnroll 16-byte vectors per trip, the workgroups
+// striding over the buffer; the XOR of everything read goes to one word per
+// workgroup so that no load is dead.
+__global__ void __launch_bounds__(kStreamThreads)
+    probe_stream_read_kernel(const u32x4* __restrict__ src, size_t n_vec,
+                             unsigned* __restrict__ sink) {
+  const size_t stride = (size_t)gridDim.x * kStreamThreads * kStreamUnroll;
+  u32x4 acc = {0u, 0u, 0u, 0u};
+  size_t i = (size_t)blockIdx.x * kStreamThreads * kStreamUnroll + threadIdx.x;
+  for (; i + (size_t)(kStreamUnroll - 1) * kStreamThreads < n_vec; i += stride) {
+    u32x4 v[kStreamUnroll];
+#pragma unroll
+    for (int u = 0; u < kStreamUnroll; ++u)
+      v[u] = __builtin_nontemporal_load(src + i + (size_t)u * kStreamThreads);
+#pragma unroll
+    for (int u = 0; u < kStreamUnroll; ++u) acc ^= v[u];
+  }
+  // the ragged end: this lane's remaining positions of its last group (every
+  // later group starts past the end, since stride > (kStreamUnroll - 1) * threads)
+#pragma unroll
+  for (int u = 0; u < kStreamUnroll - 1; ++u)
+    if (i + (size_t)u * kStreamThreads < n_vec) acc ^= src[i + (size_t)u * kStreamThreads];
+  __shared__ unsigned red[kStreamThreads];
+  red[threadIdx.x] = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    unsigned x = 0;
+    for (int t = 0; t < kStreamThreads; ++t) x ^= red[t];
+    sink[blockIdx.x] = x;
+  }
+}
+
+constexpr int kMfmaThreads = 512;  // 8 waves: two per SIMD
+constexpr int kMfmaChains = 4;     // independent accumulators per wave
+
+// iters x kMfmaChains matrix instructions per wave.  Block 0, thread 0 also
+// records the shader-clock and real-time counters around its loop.
+__global__ void __launch_bounds__(kMfmaThreads)
+    probe_mfma_kernel(int iters, float* __restrict__ sink, unsigned long long* __restrict__ clk) {
+  const int lane = threadIdx.x & 63;
+  pbf16x8 a, b;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    a[k] = (__bf16)(0.001f * (float)(lane + k));
+    b[k] = (__bf16)(0.002f * (float)(lane - k));
+  }
+  pf32x4 c[kMfmaChains];
+#pragma unroll
+  for (int k = 0; k < kMfmaChains; ++k) c[k] = pf32x4{0.f, 0.f, 0.f, 0.f};
+  unsigned long long t0 = 0, r0 = 0;
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    t0 = __builtin_readcyclecounter();
+    r0 = __builtin_amdgcn_s_memrealtime();
+  }
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int k = 0; k < kMfmaChains; ++k)
+      c[k] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c[k], 0, 0, 0);
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int k = 0; k < kMfmaChains; ++k) s += c[k][0] + c[k][1] + c[k][2] + c[k][3];
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    const unsigned long long t1 = __builtin_readcyclecounter();
+    const unsigned long long r1 = __builtin_amdgcn_s_memrealtime();
+    clk[0] = t1 - t0;
+    clk[1] = r1 - r0;
+  }
+  sink[(size_t)blockIdx.x * kMfmaThreads + threadIdx.x] = s;
+}
+
+}  // namespace mla
+
+extern "C" hipError_t mla_launch_probe_stream_read(const void* src, size_t bytes, unsigned* sink,
+                                                   int blocks, hipStream_t stream) {
+  hipLaunchKernelGGL(mla::probe_stream_read_kernel, dim3(blocks), dim3(mla::kStreamThreads), 0,
+                     stream, (const mla::u32x4*)src, bytes / 16, sink);
+  return hipGetLastError();
+}
+
+extern "C" hipError_t mla_launch_probe_mfma(int iters, int blocks, float* sink,
+                                            unsigned long long* clk, hipStream_t stream) {
+  hipLaunchKernelGGL(mla::probe_mfma_kernel, dim3(blocks), dim3(mla::kMfmaThreads), 0, stream,
+                     iters, sink, clk);
+  return hipGetLastError();
+}

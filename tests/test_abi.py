@@ -60,6 +60,19 @@ def test_status_strings(lib):
     for code, text in [(0, "ok"), (1, "invalid argument"), (2, "unsupported shape"),
                        (3, "workspace too small"), (4, "HIP runtime error")]:
         assert lib.mla_status_string(code).decode() == text
+    assert "debug checks" in lib.mla_status_string(5).decode()
+
+
+def test_debug_switch(lib):
+    """mla_set_debug_checks returns the previous setting; -1 only reads it."""
+    lib.mla_set_debug_checks.argtypes = [ctypes.c_int32]
+    lib.mla_set_debug_checks.restype = ctypes.c_int32
+    first = lib.mla_set_debug_checks(-1)
+    assert first in (0, 1)
+    assert lib.mla_set_debug_checks(1) == first
+    assert lib.mla_set_debug_checks(-1) == 1
+    assert lib.mla_set_debug_checks(0) == 1
+    assert lib.mla_set_debug_checks(first) == 0
 
 
 def test_partitions_and_sizes(lib):

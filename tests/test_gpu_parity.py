@@ -84,25 +84,36 @@ def compare(out, lse, ref_out, ref_lse, batches=None):
 
 
 # ---------------------------------------------------------------- the five workloads
-@pytest.mark.parametrize("k", [1, 2, 3, 5])
+def _report(name, case, errs):
+    """Append one workload's errors to the file named by MLA_PARITY_REPORT
+    (a summary of how far inside the gates each workload sits)."""
+    path = os.environ.get("MLA_PARITY_REPORT")
+    if not path:
+        return
+    import json
+
+    rec = {"workload": name, "batch": case.batch, "s_q": case.s_q, "h_q": case.h_q,
+           "causal": bool(case.causal), "sum_seqlen": int(case.cache_seqlens.sum()),
+           "out_max_abs_err": errs[0], "out_normwise_rel_err": errs[1],
+           "lse_max_abs_err": errs[2], "gates": {"out_atol": OUT_ATOL, "out_rtol": OUT_RTOL,
+                                                 "out_norm_rtol": OUT_NORM_RTOL,
+                                                 "lse_atol": LSE_ATOL}}
+    with open(path, "a") as fh:
+        fh.write(json.dumps(rec) + "\n")
+
+
+@pytest.mark.parametrize("k", [1, 2, 3, 4, 5])
 def test_config_full_parity(mla, k):
+    """Every row of every sequence of the five workloads against the oracle,
+    with unused pool pages and the tail slots of every last page poisoned
+    with NaN (the kernels must never read them)."""
     _say(f"[parity] workload {k}: full oracle")
     case = make_config_case(k, poison_unused=True, poison_tail=True)
     out, lse = run(mla, case)
     ref_out, ref_lse = oracle.decode_ref(case)
     errs = compare(out, lse, ref_out, ref_lse)
     _say(f"[parity] workload {k}: max|err| {errs[0]:.2e} norm {errs[1]:.2e} lse {errs[2]:.2e}")
-
-
-def test_config4_sampled_parity(mla):
-    _say("[parity] workload 4: sampled batches")
-    case = make_config_case(4)
-    out, lse = run(mla, case)
-    L = case.cache_seqlens
-    pick = sorted({int(np.argmin(L)), int(np.argmax(L)), 0, 63, 127, 5, 77, 101})
-    ref_out, ref_lse = oracle.decode_ref(case, batches=pick)
-    errs = compare(out, lse, ref_out, ref_lse, batches=pick)
-    _say(f"[parity] workload 4 batches {pick}: {errs}")
+    _report(k, case, errs)
 
 
 def test_batch_at_the_limit(mla):

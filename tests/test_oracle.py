@@ -188,6 +188,103 @@ def test_single_query_causal_equals_noncausal():
     assert np.array_equal(oa, ob) and np.array_equal(la, lb)
 
 
+# ---------------------------------------------------------------- single rows
+# rows (b, i, h) chosen so that a swapped (i, h), a wrong query index handed to
+# the causal mask or a stale cached sequence changes the result
+_ROW_CASES = [
+    # lengths, s_q, h_q, causal
+    ([130, 0, 65, 3], 3, 2, True),
+    ([70, 64, 1], 2, 3, True),
+    ([129, 5], 3, 2, False),
+]
+
+
+def _all_rows(case, order_seed=None):
+    rows = [(b, i, h) for b in range(case.batch) for i in range(case.s_q) for h in range(case.h_q)]
+    if order_seed is not None:  # jump between sequences, so the gather cache is refreshed
+        rng = np.random.Generator(np.random.PCG64(order_seed))
+        rows = [rows[k] for k in rng.permutation(len(rows))]
+    return rows
+
+
+@pytest.mark.parametrize("seqlens,s_q,h_q,causal", _ROW_CASES)
+def test_rows_match_bruteforce(seqlens, s_q, h_q, causal):
+    """Every row of decode_ref_rows against the scalar brute force (its own
+    loops, its own position walk and block-table lookups), rows visited in a
+    shuffled order; the empty sequence gives 0 / -inf."""
+    case = _tiny(seqlens, s_q, h_q, causal, seed=121 + s_q * h_q, pool_factor=1.25)
+    o_bf, l_bf = oracle.decode_bruteforce(case)
+    rows = _all_rows(case, order_seed=5)
+    got = oracle.decode_ref_rows(case, rows)
+    for (b, i, h), (o, l) in zip(rows, got):
+        if math.isinf(l_bf[b, i, h]):
+            assert math.isinf(l) and l < 0 and np.all(o == 0.0), (b, i, h)
+            continue
+        assert abs(l - l_bf[b, i, h]) <= 1e-12, (b, i, h)
+        assert np.max(np.abs(o - o_bf[b, i, h])) <= 1e-12, (b, i, h)
+
+
+@pytest.mark.parametrize("seqlens,s_q,h_q,causal", _ROW_CASES)
+def test_rows_match_whole_reference(seqlens, s_q, h_q, causal):
+    """decode_ref_rows equals decode_ref row for row (the same definition,
+    one row at a time instead of one sequence at a time)."""
+    case = _tiny(seqlens, s_q, h_q, causal, seed=131 + s_q, pool_factor=1.25)
+    o_ref, l_ref = oracle.decode_ref(case)
+    rows = _all_rows(case)
+    got = oracle.decode_ref_rows(case, rows)
+    for (b, i, h), (o, l) in zip(rows, got):
+        if math.isinf(l_ref[b, i, h]):
+            assert math.isinf(l) and np.all(o == 0.0)
+            continue
+        assert abs(l - l_ref[b, i, h]) <= 1e-12
+        assert np.max(np.abs(o - o_ref[b, i, h])) <= 1e-12
+
+
+def test_rows_distinguish_token_and_head():
+    """Rows (b, i, h) and (b, h, i) of a causal case differ, so a swapped
+    index cannot pass unnoticed."""
+    case = _tiny([90], 3, 3, True, seed=141)
+    a = oracle.decode_ref_rows(case, [(0, 0, 2)])[0]
+    b = oracle.decode_ref_rows(case, [(0, 2, 0)])[0]
+    assert abs(a[1] - b[1]) > 1e-3
+
+
+def test_planted_row_index_swap_is_caught(monkeypatch):
+    """decode_ref_rows reading q[b, h, i] instead of q[b, i, h] fails the
+    brute-force pin."""
+    good = mla_oracle.decode_ref_rows
+
+    def bad(case, rows):
+        return good(case, [(b, h, i) if h < case.s_q and i < case.h_q else (b, i, h)
+                           for (b, i, h) in rows])
+
+    monkeypatch.setattr(oracle, "decode_ref_rows", bad)
+    with pytest.raises(AssertionError):
+        test_rows_match_bruteforce([130, 0, 65, 3], 3, 2, True)
+
+
+def test_planted_row_mask_index_is_caught(monkeypatch):
+    """A causal mask taken for the head index instead of the query token
+    fails the brute-force pin."""
+    good_vis = mla_oracle.visible_tokens
+    calls = {"n": 0}
+
+    def bad_rows(case, rows):
+        out = []
+        for (b, i, h) in rows:
+            monkeypatch.setattr(mla_oracle, "visible_tokens",
+                                lambda L, s_q, _i, c, hh=h: good_vis(L, s_q, min(hh, s_q - 1), c))
+            out += mla_oracle.decode_ref_rows(case, [(b, i, h)])
+            monkeypatch.setattr(mla_oracle, "visible_tokens", good_vis)
+            calls["n"] += 1
+        return out
+
+    monkeypatch.setattr(oracle, "decode_ref_rows", bad_rows)
+    with pytest.raises(AssertionError):
+        test_rows_match_bruteforce([70, 64, 1], 2, 3, True)
+    assert calls["n"] > 0
+
+
 # ---------------------------------------------------------------- split + merge
 @pytest.mark.parametrize("seed", [1, 2, 3])
 def test_split_and_merge_equals_unsplit(seed):
