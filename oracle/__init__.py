@@ -22,4 +22,5 @@ from .mla_oracle import (  # noqa: F401
     merge_partials,
     kv_append_ref,
 )
-from . import fp8_cache  # noqa: F401  (FP8 latent cache: format, quantize, dequantize)
+from . import fp8_cache  # noqa: F401
+from . import prefill  # noqa: F401  (MLA prefill, per-head form)  (FP8 latent cache: format, quantize, dequantize)

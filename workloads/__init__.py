@@ -22,4 +22,6 @@ from .gen import (  # noqa: F401
     ROPE_DIM,
     AppendCase,
     make_append_case,
+    PrefillCase,
+    make_prefill_case,
 )

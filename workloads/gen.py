@@ -317,3 +317,50 @@ def make_append_case(seqlens: Sequence[int], n_new: int, free: int, seed: int,
     free_pages = perm[k:k + free].copy()
     new_kv = bf16_bits_from_f32(rng.standard_normal((batch, n_new, HEAD_DIM), dtype=np.float32))
     return AppendCase(kv, bt, np.array(seqlens, dtype=np.int32), new_kv, free_pages)
+
+
+# --------------------------------------------------------------------------
+# inputs of MLA prefill (per-head form)
+# --------------------------------------------------------------------------
+@dataclass
+class PrefillCase:
+    """Packed prompts: sequence s holds tokens cu_seqlens[s] .. cu_seqlens[s+1]-1.
+    Raw bf16 bits throughout."""
+    cu_seqlens: np.ndarray  # int32 [batch + 1]
+    latent: np.ndarray      # uint16 [T, 576]: the cache entry [c (512) ; r (64)] of each token
+    q: np.ndarray           # uint16 [T, H, 192]: [q_nope (128) ; q_rope (64)] per head
+    w_uk: np.ndarray        # uint16 [H, 128, 512]: W_UK,h
+    w_uv: np.ndarray        # uint16 [H, 128, 512]: W_UV,h
+    softmax_scale: float
+
+    @property
+    def tokens(self) -> int:
+        return int(self.latent.shape[0])
+
+    @property
+    def heads(self) -> int:
+        return int(self.q.shape[1])
+
+
+def make_prefill_case(seqlens: Sequence[int], h_q: int, seed: int,
+                      softmax_scale: Optional[float] = None) -> PrefillCase:
+    """Draw, in this order from PCG64(seed): the latents [c ; r] ~ N(0, 1),
+    the queries ~ N(0, 1), W_UK then W_UV ~ N(0, 1/512) (so a widened key
+    or value entry has variance about 1)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    seqlens = [int(x) for x in seqlens]
+    if any(x < 0 for x in seqlens) or not seqlens:
+        raise ValueError("lengths must be non-negative, at least one sequence")
+    cu = np.zeros(len(seqlens) + 1, dtype=np.int32)
+    cu[1:] = np.cumsum(seqlens)
+    T = int(cu[-1])
+
+    def draw(shape, sd=1.0):
+        return bf16_bits_from_f32(rng.standard_normal(shape, dtype=np.float32) * np.float32(sd))
+
+    latent = draw((T, HEAD_DIM))
+    q = draw((T, h_q, NOPE_DIM + ROPE_DIM))
+    w_uk = draw((h_q, NOPE_DIM, V_DIM), 1.0 / math.sqrt(V_DIM))
+    w_uv = draw((h_q, NOPE_DIM, V_DIM), 1.0 / math.sqrt(V_DIM))
+    scale = default_scale() if softmax_scale is None else float(np.float32(softmax_scale))
+    return PrefillCase(cu, latent, q, w_uk, w_uv, scale)
