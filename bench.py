@@ -508,6 +508,59 @@ def kv_append_rates(mla, seqlens, n_new, seed, dev, R=32):
             "hbm_frac": round(gbs / HBM_PEAK_GBS, 5), "launches_per_call": 2}
 
 
+def prefill_rates(mla, seqlens, h_q, seed, dev, reps=5):
+    """Time MLA prefill in per-head form on packed prompts: the expansion of
+    the latents into per-head keys and values (two launches) and the causal
+    attention, each alone, HIP events on the launch stream around a graph of
+    back-to-back launches.  Attention flops: 2 * (192 + 128) per (query,
+    visible key) pair and head; expansion: 2 * 512 * 128 * 2 per token and
+    head."""
+    import torch
+    from workloads import make_prefill_case
+
+    case = make_prefill_case(seqlens, h_q, seed)
+    up = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(  # noqa
+        torch.bfloat16)
+    lat, q, wk, wv = up(case.latent), up(case.q), up(case.w_uk), up(case.w_uv)
+    cu = torch.from_numpy(case.cu_seqlens).to(dev)
+    T = case.tokens
+    k_nope = torch.empty((T, h_q, 128), dtype=torch.bfloat16, device=dev)
+    v = torch.empty_like(k_nope)
+    o = torch.empty_like(k_nope)
+    lse = torch.empty((T, h_q), dtype=torch.float32, device=dev)
+    ms = int(max(seqlens))
+    L = np.asarray(seqlens, dtype=np.int64)
+    pairs = int((L * (L + 1) // 2).sum())
+    att_flops = 2 * (192 + 128) * h_q * pairs
+    exp_flops = 2 * 2 * 512 * 128 * h_q * T
+
+    def expand():
+        mla.prefill_expand_kv(lat, wk, wv, k_nope, v)
+
+    def attend():
+        mla.prefill_attention(q, k_nope, lat[:, 512:], v, cu, ms, case.softmax_scale, True, o, lse)
+
+    out = {"prompts": [int(x) for x in seqlens], "heads": h_q, "tokens": T}
+    for name, fn, fl in (("expand_kv", expand, exp_flops), ("attention", attend, att_flops)):
+        fn()
+        torch.cuda.synchronize()
+        g = _capture(lambda: [fn() for _ in range(reps)])
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        ts = []
+        for _ in range(3):
+            e0.record()
+            g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) / reps)
+        t = float(np.median(ts))
+        tf = fl / (t * 1e-3) / 1e12
+        out[name] = {"us": round(t * 1e3, 2), "flops": int(fl), "TFLOP_per_s": round(tf, 1),
+                     "mfma_frac": round(tf / BF16_PEAK_TFLOPS, 4)}
+    return out
+
+
 def copy_calibration(mib, launches=5):
     """Plain device-to-device copies of a known size, for scaling the HBM byte
     counters (run under rocprofv3 --pmc)."""
@@ -925,6 +978,8 @@ def main():
                     mla, [int(x) for x in c2.cache_seqlens], 4, 16, 4002, dev),
                 "chunk_512x128": query_token_rates(mla, [4096], 512, 128, 4003, dev),
             },
+            # MLA prefill in per-head form: one 4096-token prompt at 128 heads
+            "prefill": prefill_rates(mla, [4096], 128, 5001, dev),
         }
     if not args.no_cpu_baseline:
         print("# timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)

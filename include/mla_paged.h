@@ -91,6 +91,7 @@ typedef enum {
 #define MLA_MAX_APPEND 65536 /* new tokens per sequence in one mla_kv_append */
 #define MLA_MAX_FUSED_BATCH 1024 /* sequences for a decode that schedules itself */
 #define MLA_FP8_TOKEN_BYTES 656  /* one token of the FP8 latent cache (see mla_kv_quantize_fp8) */
+#define MLA_MAX_PREFILL_HEADS 65535 /* heads of one mla_prefill_attention / mla_prefill_expand_kv */
 
 /*
  * Debug checks of device contents before every mla_decode_paged /
@@ -292,6 +293,54 @@ mla_status_t mla_decode_paged_fp8(const void* q, const void* kv_fp8, const int32
                                   const int32_t* tile_metadata, int32_t* num_splits,
                                   int32_t num_cus, void* workspace, size_t workspace_bytes,
                                   void* out, float* lse, hipStream_t stream);
+
+/*
+ * MLA prefill, per-head form: the stage before decoding, run separately
+ * from it (DeepSeek-V3 summary, paragraph on inference speed; FlashMLA
+ * itself is a decode kernel, release note introduction).  For a whole
+ * prompt the latent is widened per head first (release note, paragraph on
+ * the MLA core principles): head h's key of token t is [W_UK,h c_t ; r_t]
+ * and its value W_UV,h c_t, with c_t the 512-value latent and r_t the
+ * 64-value rotary key shared by every head.
+ *
+ * mla_prefill_expand_kv widens the latents:
+ *   latent  bf16 [tokens][latent_stride]: c_t = latent[t][0:512] (a cache
+ *           entry [c ; r] has latent_stride 576); latent_stride >= 512, a
+ *           multiple of 8
+ *   w_uk, w_uv  bf16 [h_q][128][512]: W_UK,h and W_UV,h as stored
+ *   k_nope  bf16 [tokens][h_q][128]: k_nope[t][h] = W_UK,h c_t
+ *   v       bf16 [tokens][h_q][128]: v[t][h] = W_UV,h c_t
+ * fp32 accumulation, one rounding to bf16 (nearest even).  Two launches.
+ *
+ * mla_prefill_attention: packed prompts, prompt s holding tokens
+ * cu_seqlens[s] .. cu_seqlens[s+1] - 1 (cu_seqlens int32 [batch + 1],
+ * device, non-decreasing from 0; max_seqlen >= the longest prompt, host).
+ *   q       bf16 [tokens][h_q][192]: [q_nope (128) ; q_rope (64)] per head,
+ *           rotary embedding already applied
+ *   k_nope  bf16 [tokens][h_q][128], v bf16 [tokens][h_q][128]
+ *   k_rope  bf16: row t at k_rope + t * rope_stride, 64 values (for the
+ *           cache entries [c ; r]: k_rope = latent + 512, rope_stride 576);
+ *           rope_stride >= 64, a multiple of 8
+ *   o       bf16 [tokens][h_q][128]: sum_u exp(s_u - lse) v[u][h]
+ *   lse     fp32 [tokens][h_q]: ln sum_u exp(s_u), natural log
+ * with s_u = softmax_scale * dot(q[t][h], [k_nope[u][h] ; k_rope[u]]) over
+ * the keys u of t's prompt at or before t (causal != 0) or all of them.
+ * fp32 scores and accumulators, bf16 weights in the value product, out
+ * rounded once to bf16.  softmax_scale finite and positive.  All pointers
+ * device, 16-byte aligned, caller-owned; asynchronous on `stream`; nothing
+ * allocated.  Errors: MLA_ERR_INVALID_ARGUMENT (null or misaligned pointer,
+ * sizes or strides out of range, bad scale), MLA_ERR_UNSUPPORTED (batch >
+ * MLA_MAX_BATCH, h_q > MLA_MAX_PREFILL_HEADS, or tokens * h_q * 128 >= 2^31
+ * for the expansion), MLA_ERR_HIP.  cu_seqlens contents are a precondition.
+ */
+mla_status_t mla_prefill_expand_kv(const void* latent, int32_t latent_stride, int32_t tokens,
+                                   const void* w_uk, const void* w_uv, int32_t h_q, void* k_nope,
+                                   void* v, hipStream_t stream);
+mla_status_t mla_prefill_attention(const void* q, const void* k_nope, const void* k_rope,
+                                   int32_t rope_stride, const void* v,
+                                   const int32_t* cu_seqlens, int32_t batch, int32_t h_q,
+                                   int32_t max_seqlen, float softmax_scale, int32_t causal,
+                                   void* o, float* lse, hipStream_t stream);
 
 /*
  * Machine-limit probes (benchmark instruments, not part of the decode).

@@ -41,6 +41,8 @@ __all__ = [
     "mla_decode_fp8",
     "FP8_TOKEN_BYTES",
     "set_debug_checks",
+    "prefill_expand_kv",
+    "prefill_attention",
 ]
 
 HEAD_DIM = 576
@@ -108,6 +110,11 @@ def load_library() -> ctypes.CDLL:
     lib.mla_probe_stream_read.restype = ctypes.c_int
     lib.mla_probe_mfma.argtypes = [i32, i32, vp, vp, vp]
     lib.mla_probe_mfma.restype = ctypes.c_int
+    lib.mla_prefill_expand_kv.argtypes = [vp, i32, i32, vp, vp, i32, vp, vp, vp]
+    lib.mla_prefill_expand_kv.restype = ctypes.c_int
+    lib.mla_prefill_attention.argtypes = [vp, vp, vp, i32, vp, vp, i32, i32, i32, f32, i32, vp,
+                                          vp, vp]
+    lib.mla_prefill_attention.restype = ctypes.c_int
     lib.mla_set_debug_checks.argtypes = [i32]
     lib.mla_set_debug_checks.restype = i32
     lib.mla_status_string.argtypes = [ctypes.c_int]
@@ -321,6 +328,66 @@ def mla_decode(q, kv_cache, block_table, cache_seqlens, softmax_scale, causal, n
                                 meta, splits, num_cus, stream=stream)
     combine(ws, splits, batch, s_q, h_q, out, lse, num_cus, stream)
     return out, lse
+
+
+def prefill_expand_kv(latent: torch.Tensor, w_uk: torch.Tensor, w_uv: torch.Tensor,
+                      k_nope: Optional[torch.Tensor] = None, v: Optional[torch.Tensor] = None,
+                      stream=None):
+    """Widen the latents per head for prefill: ``latent [T, >=512]`` (c_t =
+    the first 512 values of row t), ``w_uk`` and ``w_uv [h, 128, 512]`` ->
+    ``k_nope[t, h] = W_UK,h c_t`` and ``v[t, h] = W_UV,h c_t``, each
+    ``[T, h, 128]``."""
+    if latent.dim() != 2 or latent.dtype != torch.bfloat16 or latent.stride(1) != 1:
+        raise ValueError("latent must be a bf16 [T, >=512] matrix with unit column stride")
+    _need(w_uk, "w_uk", torch.bfloat16, 3)
+    _need(w_uv, "w_uv", torch.bfloat16, 3)
+    T = latent.shape[0]
+    h_q = w_uk.shape[0]
+    if tuple(w_uk.shape) != (h_q, NOPE_DIM, V_DIM) or tuple(w_uv.shape) != (h_q, NOPE_DIM, V_DIM):
+        raise ValueError("w_uk and w_uv must be [h, 128, 512]")
+    dev = latent.device
+    if k_nope is None:
+        k_nope = torch.empty((T, h_q, NOPE_DIM), dtype=torch.bfloat16, device=dev)
+    if v is None:
+        v = torch.empty((T, h_q, NOPE_DIM), dtype=torch.bfloat16, device=dev)
+    _need(k_nope, "k_nope", torch.bfloat16, 3)
+    _need(v, "v", torch.bfloat16, 3)
+    _check("mla_prefill_expand_kv", load_library().mla_prefill_expand_kv(
+        _ptr(latent), latent.stride(0), T, _ptr(w_uk), _ptr(w_uv), h_q, _ptr(k_nope), _ptr(v),
+        _stream(stream)))
+    return k_nope, v
+
+
+def prefill_attention(q: torch.Tensor, k_nope: torch.Tensor, k_rope: torch.Tensor,
+                      v: torch.Tensor, cu_seqlens: torch.Tensor, max_seqlen: int,
+                      softmax_scale: float, causal: bool = True,
+                      o: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                      stream=None):
+    """Per-head attention over packed prompts: ``q [T, h, 192]``, ``k_nope``
+    and ``v [T, h, 128]``, ``k_rope [T, 64]`` (any row stride, e.g. the last
+    64 values of the cache entries), ``cu_seqlens [batch + 1]`` int32.
+    Returns ``(o [T, h, 128], lse [T, h])``."""
+    _need(q, "q", torch.bfloat16, 3)
+    _need(k_nope, "k_nope", torch.bfloat16, 3)
+    _need(v, "v", torch.bfloat16, 3)
+    _need(cu_seqlens, "cu_seqlens", torch.int32, 1)
+    if k_rope.dim() != 2 or k_rope.dtype != torch.bfloat16 or k_rope.stride(1) != 1 or \
+            k_rope.shape[1] != ROPE_DIM:
+        raise ValueError("k_rope must be a bf16 [T, 64] matrix with unit column stride")
+    T, h_q, d = q.shape
+    if d != NOPE_DIM + ROPE_DIM or tuple(k_nope.shape) != (T, h_q, NOPE_DIM) or \
+            tuple(v.shape) != (T, h_q, NOPE_DIM) or k_rope.shape[0] != T:
+        raise ValueError("q [T,h,192], k_nope / v [T,h,128] and k_rope [T,64] must agree")
+    dev = q.device
+    if o is None:
+        o = torch.empty((T, h_q, NOPE_DIM), dtype=torch.bfloat16, device=dev)
+    if lse is None:
+        lse = torch.empty((T, h_q), dtype=torch.float32, device=dev)
+    _check("mla_prefill_attention", load_library().mla_prefill_attention(
+        _ptr(q), _ptr(k_nope), _ptr(k_rope), k_rope.stride(0), _ptr(v), _ptr(cu_seqlens),
+        cu_seqlens.shape[0] - 1, h_q, int(max_seqlen), float(softmax_scale), int(bool(causal)),
+        _ptr(o), _ptr(lse), _stream(stream)))
+    return o, lse
 
 
 def absorb_query(q_nope: torch.Tensor, q_rope: torch.Tensor, w_uk_t: torch.Tensor,

@@ -39,7 +39,7 @@ constexpr int kRowChunk = 256;   // rows per workgroup (blockIdx.x)
 
 template <int K, int NCOL, int D>
 __global__ void __launch_bounds__(256, 2) absorb_kernel(const uint16_t* __restrict__ act,
-                                                     int act_stride,
+                                                     int act_row, int act_head,
                                                      const uint16_t* __restrict__ w,
                                                      uint16_t* __restrict__ out, int out_stride,
                                                      int M, int H, int N,
@@ -66,7 +66,7 @@ __global__ void __launch_bounds__(256, 2) absorb_kernel(const uint16_t* __restri
   auto load_tile = [&](int t, bf16x8 (&af)[KS]) __attribute__((always_inline)) {
     int m = m_begin + 16 * t + l16;
     m = m < m_end ? m : m_begin;
-    const uint16_t* a = act + ((size_t)m * H + h) * act_stride + 8 * g;
+    const uint16_t* a = act + (size_t)m * act_row + (size_t)h * act_head + 8 * g;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) af[ks] = *(const bf16x8*)(a + 32 * ks);
   };
@@ -191,7 +191,7 @@ extern "C" hipError_t mla_launch_absorb_query(const uint16_t* q_c, const uint16_
   // 256 columns (a 64 KiB slice of W) per workgroup
   const dim3 grid((M + kRowChunk - 1) / kRowChunk, kDv / 256, H);
   hipLaunchKernelGGL((absorb_kernel<kNope, 256, kQueryDepth>), grid, dim3(256), 0, stream, q_c,
-                     kNope, w_uk_t, q_out, kD, M, H, kDv, q_r, kRope);
+                     H * kNope, kNope, w_uk_t, q_out, kD, M, H, kDv, q_r, kRope);
   return hipGetLastError();
 }
 
@@ -202,6 +202,26 @@ extern "C" hipError_t mla_launch_absorb_output(const uint16_t* lat_out, const ui
   // 64 columns (a 64 KiB slice of W) per workgroup
   const dim3 grid((M + kRowChunk - 1) / kRowChunk, kNope / 64, H);
   hipLaunchKernelGGL((absorb_kernel<kDv, 64, kOutputDepth>), grid, dim3(256), 0, stream, lat_out,
-                     kDv, w_uv, o, kNope, M, H, kNope, (const uint16_t*)nullptr, 0);
+                     H * kDv, kDv, w_uv, o, kNope, M, H, kNope, (const uint16_t*)nullptr, 0);
+  return hipGetLastError();
+}
+
+// Prefill: every head's key (latent part) and value widened from the shared
+// latent of each token, k_nope[t, h, :] = W_UK,h c_t and v[t, h, :] = W_UV,h c_t
+// (the same product with the activation row shared by the heads: head
+// stride 0).  c_t is the first 512 values of row t of `latent` (row stride
+// latent_stride values).
+extern "C" hipError_t mla_launch_prefill_expand(const uint16_t* latent, int latent_stride, int T,
+                                                const uint16_t* w_uk, const uint16_t* w_uv, int H,
+                                                uint16_t* k_nope, uint16_t* v, hipStream_t stream) {
+  using namespace mla;
+  const dim3 grid((T + kRowChunk - 1) / kRowChunk, kNope / 64, H);
+  hipLaunchKernelGGL((absorb_kernel<kDv, 64, kOutputDepth>), grid, dim3(256), 0, stream, latent,
+                     latent_stride, 0, w_uk, k_nope, kNope, T, H, kNope, (const uint16_t*)nullptr,
+                     0);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((absorb_kernel<kDv, 64, kOutputDepth>), grid, dim3(256), 0, stream, latent,
+                     latent_stride, 0, w_uv, v, kNope, T, H, kNope, (const uint16_t*)nullptr, 0);
   return hipGetLastError();
 }

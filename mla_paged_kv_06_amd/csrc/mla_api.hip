@@ -21,6 +21,11 @@ extern "C" hipError_t mla_launch_probe_stream_read(const void* src, size_t bytes
                                                    int blocks, hipStream_t stream);
 extern "C" hipError_t mla_launch_probe_mfma(int iters, int blocks, float* sink,
                                             unsigned long long* clk, hipStream_t stream);
+extern "C" hipError_t mla_launch_prefill_expand(const uint16_t* latent, int latent_stride, int T,
+                                                const uint16_t* w_uk, const uint16_t* w_uv, int H,
+                                                uint16_t* k_nope, uint16_t* v, hipStream_t stream);
+extern "C" hipError_t mla_launch_prefill_attention(const mla::PrefillParams* prm, int batch,
+                                                   int max_seqlen, hipStream_t stream);
 extern "C" hipError_t mla_launch_sched(const int32_t* seqlens, int batch, int num_parts, int c0,
                                        int32_t* meta, int32_t* splits, hipStream_t stream);
 
@@ -362,6 +367,54 @@ mla_status_t mla_kv_append(void* kv_cache, int32_t num_pages, int32_t* block_tab
   hipError_t e = mla_launch_kv_append((uint16_t*)kv_cache, block_table, max_pages, cache_seqlens,
                                       batch, (const uint16_t*)new_kv, n_new, free_pages,
                                       free_count, status, stream);
+  return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+mla_status_t mla_prefill_expand_kv(const void* latent, int32_t latent_stride, int32_t tokens,
+                                   const void* w_uk, const void* w_uv, int32_t h_q, void* k_nope,
+                                   void* v, hipStream_t stream) {
+  if (!latent || !w_uk || !w_uv || !k_nope || !v) return MLA_ERR_INVALID_ARGUMENT;
+  if (tokens <= 0 || h_q <= 0 || latent_stride < MLA_V_DIM || (latent_stride & 7))
+    return MLA_ERR_INVALID_ARGUMENT;
+  if (((uintptr_t)latent | (uintptr_t)w_uk | (uintptr_t)w_uv | (uintptr_t)k_nope |
+       (uintptr_t)v) & 15)
+    return MLA_ERR_INVALID_ARGUMENT;
+  if (h_q > MLA_MAX_PREFILL_HEADS || (long long)tokens * h_q * MLA_NOPE_DIM >= (1LL << 31))
+    return MLA_ERR_UNSUPPORTED;
+  const hipError_t e = mla_launch_prefill_expand((const uint16_t*)latent, latent_stride, tokens,
+                                                 (const uint16_t*)w_uk, (const uint16_t*)w_uv,
+                                                 h_q, (uint16_t*)k_nope, (uint16_t*)v, stream);
+  return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+mla_status_t mla_prefill_attention(const void* q, const void* k_nope, const void* k_rope,
+                                   int32_t rope_stride, const void* v,
+                                   const int32_t* cu_seqlens, int32_t batch, int32_t h_q,
+                                   int32_t max_seqlen, float softmax_scale, int32_t causal,
+                                   void* o, float* lse, hipStream_t stream) {
+  if (!q || !k_nope || !k_rope || !v || !cu_seqlens || !o || !lse)
+    return MLA_ERR_INVALID_ARGUMENT;
+  if (batch <= 0 || h_q <= 0 || max_seqlen < 0 || rope_stride < MLA_ROPE_DIM ||
+      (rope_stride & 7))
+    return MLA_ERR_INVALID_ARGUMENT;
+  if (!std::isfinite(softmax_scale) || !(softmax_scale > 0.f)) return MLA_ERR_INVALID_ARGUMENT;
+  if (((uintptr_t)q | (uintptr_t)k_nope | (uintptr_t)k_rope | (uintptr_t)v | (uintptr_t)o) & 15)
+    return MLA_ERR_INVALID_ARGUMENT;
+  if (batch > MLA_MAX_BATCH || h_q > MLA_MAX_PREFILL_HEADS) return MLA_ERR_UNSUPPORTED;
+  if (max_seqlen == 0) return MLA_OK;
+  mla::PrefillParams prm;
+  prm.q = (const uint16_t*)q;
+  prm.k_nope = (const uint16_t*)k_nope;
+  prm.k_rope = (const uint16_t*)k_rope;
+  prm.v = (const uint16_t*)v;
+  prm.cu = cu_seqlens;
+  prm.o = (uint16_t*)o;
+  prm.lse = lse;
+  prm.rope_stride = rope_stride;
+  prm.H = h_q;
+  prm.scale_log2 = (float)((double)softmax_scale * 1.4426950408889634);
+  prm.causal = causal ? 1 : 0;
+  const hipError_t e = mla_launch_prefill_attention(&prm, batch, max_seqlen, stream);
   return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 

@@ -116,4 +116,19 @@ struct DecodeParams {
   int sched_c0;      // fixed cost of the schedule rule (kernels that schedule in-launch)
 };
 
+// Arguments of the prefill attention kernel (filled by the C ABI after its checks).
+struct PrefillParams {
+  const uint16_t* q;       // [T][H][192]
+  const uint16_t* k_nope;  // [T][H][128]
+  const uint16_t* k_rope;  // row t at k_rope + t * rope_stride, 64 values
+  const uint16_t* v;       // [T][H][128]
+  const int32_t* cu;       // [batch + 1]
+  uint16_t* o;             // [T][H][128]
+  float* lse;              // [T][H]
+  int rope_stride;
+  int H;
+  float scale_log2;
+  int causal;
+};
+
 }  // namespace mla
