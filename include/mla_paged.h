@@ -76,7 +76,8 @@ typedef enum {
   MLA_ERR_UNSUPPORTED = 2,      /* shape outside the supported limits below */
   MLA_ERR_WORKSPACE_TOO_SMALL = 3,
   MLA_ERR_HIP = 4,              /* a HIP runtime call or launch failed */
-  MLA_ERR_DEVICE_CONTENTS = 5   /* debug checks: a length or used block-table entry out of range */
+  MLA_ERR_DEVICE_CONTENTS = 5,  /* debug checks: a length or used block-table entry out of range */
+  MLA_ERR_SCRATCH_TOO_SMALL = 6 /* mla_decode_step_noalloc: the shape needs more than its scratch */
 } mla_status_t;
 
 #define MLA_HEAD_DIM 576
@@ -92,6 +93,7 @@ typedef enum {
 #define MLA_MAX_FUSED_BATCH 1024 /* sequences for a decode that schedules itself */
 #define MLA_FP8_TOKEN_BYTES 656  /* one token of the FP8 latent cache (see mla_kv_quantize_fp8) */
 #define MLA_MAX_PREFILL_HEADS 65535 /* heads of one mla_prefill_attention / mla_prefill_expand_kv */
+#define MLA_NOALLOC_SCRATCH_BYTES (64u << 20) /* static scratch of mla_decode_step_noalloc, per GPU */
 
 /*
  * Debug checks of device contents before every mla_decode_paged /
@@ -181,6 +183,31 @@ mla_status_t mla_decode_paged(const void* q, const void* kv_cache, const int32_t
 mla_status_t mla_combine(const void* workspace, size_t workspace_bytes, const int32_t* num_splits,
                          int32_t batch, int32_t s_q, int32_t h_q, int32_t num_cus, void* out,
                          float* lse, hipStream_t stream);
+
+/*
+ * One whole decode step -- the split-KV schedule, mla_decode_paged and
+ * mla_combine -- that allocates nothing and takes no workspace, for callers
+ * that cannot allocate device memory (code under graph capture, tight
+ * serving loops, harnesses that forbid allocation).  Arguments, layouts and
+ * results are those of mla_decode_paged followed by mla_combine (the
+ * schedule inside the decode where mla_decode_paged accepts a NULL
+ * tile_metadata, the separate mla_get_metadata otherwise), on the current
+ * device's compute units.  The schedule, the split counts and the split
+ * partials live in a static device array of MLA_NOALLOC_SCRATCH_BYTES
+ * (64 MiB) that each GPU running this library holds until the process ends;
+ * a shape that needs more (split counts + schedule + mla_workspace_bytes,
+ * each rounded up to 256 bytes) returns MLA_ERR_SCRATCH_TOO_SMALL and
+ * launches nothing.  Every call on one GPU shares that GPU's array, so calls
+ * that overlap on one GPU (other streams, other threads) race: the caller
+ * orders them.  Asynchronous on `stream`; no hipMalloc or hipFree, no
+ * synchronization (unless the debug checks are on).  Other errors as for
+ * mla_decode_paged.
+ */
+mla_status_t mla_decode_step_noalloc(const void* q, const void* kv_cache,
+                                     const int32_t* block_table, const int32_t* cache_seqlens,
+                                     int32_t batch, int32_t s_q, int32_t h_q, int32_t num_pages,
+                                     int32_t max_pages, float softmax_scale, int32_t causal,
+                                     void* out, float* lse, hipStream_t stream);
 
 /*
  * Query absorption, the step before mla_decode_paged.  Keys and values are

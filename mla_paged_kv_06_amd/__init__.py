@@ -41,8 +41,10 @@ __all__ = [
     "mla_decode_fp8",
     "FP8_TOKEN_BYTES",
     "set_debug_checks",
+    "decode_step_noalloc",
     "prefill_expand_kv",
     "prefill_attention",
+    "NOALLOC_SCRATCH_BYTES",
 ]
 
 HEAD_DIM = 576
@@ -51,6 +53,7 @@ PAGE_SIZE = 64
 META_INTS = 8
 MAX_FUSED_BATCH = 1024  # sequences for a decode that schedules itself
 FP8_TOKEN_BYTES = 656  # one token of the FP8 latent cache
+NOALLOC_SCRATCH_BYTES = 64 << 20  # static scratch of the no-allocation decode step, per GPU
 NOPE_DIM = 128  # per-head query part before absorption; value head width
 ROPE_DIM = 64
 
@@ -110,6 +113,9 @@ def load_library() -> ctypes.CDLL:
     lib.mla_probe_stream_read.restype = ctypes.c_int
     lib.mla_probe_mfma.argtypes = [i32, i32, vp, vp, vp]
     lib.mla_probe_mfma.restype = ctypes.c_int
+    lib.mla_decode_step_noalloc.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32,
+                                            vp, vp, vp]
+    lib.mla_decode_step_noalloc.restype = ctypes.c_int
     lib.mla_prefill_expand_kv.argtypes = [vp, i32, i32, vp, vp, i32, vp, vp, vp]
     lib.mla_prefill_expand_kv.restype = ctypes.c_int
     lib.mla_prefill_attention.argtypes = [vp, vp, vp, i32, vp, vp, i32, i32, i32, f32, i32, vp,
@@ -328,6 +334,31 @@ def mla_decode(q, kv_cache, block_table, cache_seqlens, softmax_scale, causal, n
                                 meta, splits, num_cus, stream=stream)
     combine(ws, splits, batch, s_q, h_q, out, lse, num_cus, stream)
     return out, lse
+
+
+def decode_step_noalloc(q: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Tensor,
+                        cache_seqlens: torch.Tensor, softmax_scale: float, causal: bool,
+                        out: torch.Tensor, lse: torch.Tensor, stream=None) -> None:
+    """One whole decode step (schedule, decode, combine) into the given
+    ``out`` / ``lse``, with the library's static per-GPU scratch instead of
+    a workspace: nothing is allocated.  Calls that overlap on one GPU race."""
+    _need(q, "q", torch.bfloat16, 4)
+    _need(kv_cache, "kv_cache", torch.bfloat16, 3)
+    _need(block_table, "block_table", torch.int32, 2)
+    _need(cache_seqlens, "cache_seqlens", torch.int32, 1)
+    _need(out, "out", torch.bfloat16, 4)
+    _need(lse, "lse", torch.float32, 3)
+    batch, s_q, h_q, d = q.shape
+    if d != HEAD_DIM or kv_cache.shape[1] != PAGE_SIZE or kv_cache.shape[2] != HEAD_DIM:
+        raise ValueError("q must be [b,s_q,h_q,576] and kv_cache [pages,64,576]")
+    if block_table.shape[0] != batch or cache_seqlens.shape[0] != batch:
+        raise ValueError("block_table / cache_seqlens batch mismatch")
+    if tuple(out.shape) != (batch, s_q, h_q, V_DIM) or tuple(lse.shape) != (batch, s_q, h_q):
+        raise ValueError("out must be [b,s_q,h_q,512] and lse [b,s_q,h_q]")
+    _check("mla_decode_step_noalloc", load_library().mla_decode_step_noalloc(
+        _ptr(q), _ptr(kv_cache), _ptr(block_table), _ptr(cache_seqlens), batch, s_q, h_q,
+        kv_cache.shape[0], block_table.shape[1], float(softmax_scale), int(bool(causal)),
+        _ptr(out), _ptr(lse), _stream(stream)))
 
 
 def prefill_expand_kv(latent: torch.Tensor, w_uk: torch.Tensor, w_uv: torch.Tensor,

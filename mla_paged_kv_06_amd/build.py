@@ -20,7 +20,7 @@ LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 SOURCES = ["mla_api.hip", "mla_sched.hip", "mla_decode_t16.hip", "mla_decode.hip",
            "mla_decode_sv64.hip", "mla_combine.hip", "mla_absorb.hip",
            "mla_append.hip", "mla_kv_fp8.hip", "mla_debug.hip",
-           "mla_probes.hip", "mla_prefill.hip"]
+           "mla_probes.hip", "mla_noalloc.hip", "mla_prefill.hip"]
 
 HIP_FLAGS = [
     "--offload-arch=gfx950",

@@ -445,6 +445,8 @@ const char* mla_status_string(mla_status_t status) {
     case MLA_ERR_HIP: return "HIP runtime error";
     case MLA_ERR_DEVICE_CONTENTS:
       return "cache length or block-table entry out of range (debug checks)";
+    case MLA_ERR_SCRATCH_TOO_SMALL:
+      return "shape needs more than the static scratch of the no-allocation decode";
   }
   return "unknown status";
 }
