@@ -819,6 +819,21 @@ def machine_limits(mla, dev):
             ghz.append(float(c[0]) / (float(c[1]) / 100e6) / 1e9)
     mflops = mblocks * 8 * iters * 4 * 16384
     mfma_tf = mflops / (float(np.median(ts)) * 1e-3) / 1e12
+    # LDS reads per compute unit: bytes per shader clock of workgroup 0
+    lds = {}
+    lsink = torch.empty(256 * 512, dtype=torch.int32, device=dev)
+    for kind, name, nbytes_lane in ((0, "ds_read_b128_key_fragments", 16),
+                                    (1, "ds_read_b64_tr_b16_value_fragments", 8)):
+        per_clk = []
+        for it in range(3):
+            rc = lib.mla_probe_lds(kind, 4000, 256, ctypes.c_void_p(lsink.data_ptr()),
+                                   ctypes.c_void_p(clk.data_ptr()), st())
+            torch.cuda.synchronize()
+            if rc:
+                raise RuntimeError(f"probe status {rc}")
+            if it:
+                per_clk.append(4000 * 16 * 512 * nbytes_lane / float(clk.cpu().numpy()[0]))
+        lds[name] = round(float(np.median(per_clk)), 1)
     torch.cuda.empty_cache()
     return {"stream_read_GB_per_s": round(read_gbs, 1),
             "stream_read_frac_of_spec": round(read_gbs / HBM_PEAK_GBS, 4),
@@ -826,7 +841,8 @@ def machine_limits(mla, dev):
             "mfma_loop_TFLOP_per_s": round(mfma_tf, 1),
             "mfma_loop_frac_of_spec": round(mfma_tf / BF16_PEAK_TFLOPS, 4),
             "shader_clock_GHz_under_mfma": round(float(np.median(ghz)), 3),
-            "spec_clock_GHz": 2.4}
+            "spec_clock_GHz": 2.4,
+            "lds_read_bytes_per_clock_per_cu": lds}
 
 
 def trace_stats(path):

@@ -387,6 +387,14 @@ mla_status_t mla_probe_stream_read(const void* buf, size_t bytes, void* sink, in
                                    hipStream_t stream);
 mla_status_t mla_probe_mfma(int32_t iters, int32_t blocks, void* sink, void* clocks,
                             hipStream_t stream);
+/* mla_probe_lds: `iters` x 16 LDS reads per lane by 8 waves in each of
+ * `blocks` workgroups (64 KiB of LDS each), kind 0 = 16-byte reads at the
+ * decode's key-fragment addresses, kind 1 = transposed 8-byte reads
+ * (ds_read_b64_tr_b16) at its value-fragment addresses; writes blocks * 512
+ * ints to `sink` and workgroup 0's shader-clock cycles to `clocks` (one
+ * 8-byte count), so bytes per clock per compute unit follow. */
+mla_status_t mla_probe_lds(int32_t kind, int32_t iters, int32_t blocks, void* sink, void* clocks,
+                           hipStream_t stream);
 
 /* Static, human-readable text of a status code. */
 const char* mla_status_string(mla_status_t status);

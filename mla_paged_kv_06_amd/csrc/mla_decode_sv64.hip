@@ -39,6 +39,7 @@
 
 #include "mla_decode_common.h"
 #include "mla_sched_inlaunch.h"
+#include "mla_slot_walk.h"
 
 #pragma clang diagnostic ignored "-Winline-asm"
 
@@ -171,27 +172,21 @@ __global__ void __launch_bounds__(sv::kThreadsSV, 1)
   // ---- slot stream (every wave runs the same bookkeeping on scalars)
   auto next_slot = [&](const SvSlot& s) __attribute__((always_inline)) -> SvSlot {
     SvSlot n = s;
-    if (s.h == 0) {
-      n.h = 1;
-      return n;
-    }
-    n.h = 0;
-    const int n_pages = (s.L + kPage - 1) / kPage;
-    if (s.j + 1 < (n_pages > 0 ? n_pages : 1)) {
-      n.j = uni(s.j + 1);
-    } else {
-      n.b = uni(s.b + 1);
-      n.j = 0;
-    }
-    n.valid = s.valid && item_before(Item{n.b, n.j}, eb, ej);
+    const SlotPos p = slot_next(SlotPos{s.b, s.j, s.h}, s.L);
+    n.b = uni(p.b);
+    n.j = uni(p.j);
+    n.h = p.h;
+    if (s.h == 0) return n;  // the same page: its length and entry stand
+    n.valid = s.valid && slot_before(p, eb, ej);
     if (n.valid) {
       if (n.b != s.b) n.L = load_uniform(seqlens, n.b);
       // only pages that hold tokens have a block-table entry (an empty
       // sequence's single unit holds none); the others get page 0 and a
       // resource of zero bytes
       if (is_value)
-        n.phys = n.j * kPage < n.L ? load_uniform(block_table, (size_t)n.b * prm.max_pages + n.j)
-                                   : 0;
+        n.phys = slot_page_used(n.j, n.L)
+                     ? load_uniform(block_table, (size_t)n.b * prm.max_pages + n.j)
+                     : 0;
     }
     return n;
   };
@@ -204,7 +199,7 @@ __global__ void __launch_bounds__(sv::kThreadsSV, 1)
     s0.phys = is_value ? phys0 : 0;
   } else {
     s0.L = load_uniform(seqlens, b0);
-    s0.phys = (is_value && j0 * kPage < s0.L)
+    s0.phys = (is_value && slot_page_used(j0, s0.L))
                   ? load_uniform(block_table, (size_t)b0 * prm.max_pages + j0)
                   : 0;
   }
@@ -371,8 +366,7 @@ __global__ void __launch_bounds__(sv::kThreadsSV, 1)
 
     // resource of a slot: its page's half h, bounded by the live tokens
     auto slot_rsrc = [&](const SvSlot& s) __attribute__((always_inline)) {
-      int live = s.L - s.j * kPage - s.h * kSlotTokens;
-      live = live < 0 ? 0 : (live > kSlotTokens ? kSlotTokens : live);
+      const int live = slot_live_tokens(s.j, s.h, s.L);
       return sv_rsrc(kvbase + (size_t)s.phys * kTileBytes + s.h * kSlotBytes, live * kRowBytes);
     };
     auto copy_one = [&](MLA_LDS char* buf, i32x4 rs, int k) __attribute__((always_inline)) {

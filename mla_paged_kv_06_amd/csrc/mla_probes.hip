@@ -4,7 +4,10 @@
 //     reads can reach), 16-byte loads, several in flight per lane;
 //   - a loop of independent bf16 matrix instructions, 16x16x32, with no
 //     memory traffic at all (the matrix-core ceiling), which also samples
-//     the shader clock against the constant 100 MHz real-time counter.
+//     the shader clock against the constant 100 MHz real-time counter;
+//   - LDS reads of the two kinds the decode issues: 16-byte reads of key
+//     fragments (rows 1152 bytes apart, XOR-swizzled chunks) and transposed
+//     8-byte reads of value fragments, 8 waves per compute unit.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -89,7 +92,68 @@ __global__ void __launch_bounds__(kMfmaThreads)
   sink[(size_t)blockIdx.x * kMfmaThreads + threadIdx.x] = s;
 }
 
+constexpr int kLdsProbeBytes = 65536;
+constexpr int kLdsProbeThreads = 512;
+typedef __attribute__((ext_vector_type(4))) short pi16x4;
+
+// iters x 16 LDS reads per lane, of kind kTr (0: ds_read_b128 at the decode's
+// key-fragment addresses, 1: ds_read_b64_tr_b16 at its value-fragment
+// addresses), the pattern moved by 16 bytes per trip; every address is
+// masked into the 64 KiB buffer.  Workgroup 0, thread 0 records the
+// shader-clock cycles of its loop.
+template <int kTr>
+__global__ void __launch_bounds__(kLdsProbeThreads)
+    probe_lds_kernel(int iters, int* __restrict__ sink, unsigned long long* __restrict__ clk) {
+  __shared__ __attribute__((aligned(16))) char buf[kLdsProbeBytes];
+  typedef __attribute__((address_space(3))) char lds_char;
+  const int tid = threadIdx.x, lane = tid & 63;
+  for (int i = tid; i < kLdsProbeBytes / 4; i += kLdsProbeThreads) ((int*)buf)[i] = i * 7 + 1;
+  __syncthreads();
+  const int l16 = lane & 15, g = lane >> 4;
+  int off;
+  if (kTr == 0) {
+    const int sw = l16 & 7;
+    off = l16 * 1152 + 16 * (g ^ (sw & 3)) + ((sw & 4) ? 64 : 0);
+  } else {
+    const int vt = 4 * g + (l16 >> 2);
+    off = vt * 1152 + 16 * (((l16 & 3) >> 1) ^ (vt & 7)) + 8 * (l16 & 1);
+  }
+  off += (tid >> 6) * 128;
+  constexpr int kMask = kTr == 0 ? kLdsProbeBytes - 16 : kLdsProbeBytes - 8;
+  u32x4 acc = {0u, 0u, 0u, 0u};
+  unsigned long long t0 = 0;
+  if (blockIdx.x == 0 && tid == 0) t0 = __builtin_readcyclecounter();
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const int a = (off + k * 2304) & kMask;
+      if (kTr == 0) {
+        acc ^= *(const __attribute__((address_space(3))) u32x4*)((lds_char*)buf + a);
+      } else {
+        const pi16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) pi16x4*)((lds_char*)buf + a));
+        acc.x ^= (unsigned)(unsigned short)v[0] | ((unsigned)(unsigned short)v[1] << 16);
+        acc.y ^= (unsigned)(unsigned short)v[2] | ((unsigned)(unsigned short)v[3] << 16);
+      }
+    }
+    off += 16;
+  }
+  if (blockIdx.x == 0 && tid == 0) clk[0] = __builtin_readcyclecounter() - t0;
+  sink[(size_t)blockIdx.x * kLdsProbeThreads + tid] = (int)(acc.x ^ acc.y ^ acc.z ^ acc.w);
+}
+
 }  // namespace mla
+
+extern "C" hipError_t mla_launch_probe_lds(int kind, int iters, int blocks, int* sink,
+                                           unsigned long long* clk, hipStream_t stream) {
+  if (kind == 0)
+    hipLaunchKernelGGL(mla::probe_lds_kernel<0>, dim3(blocks), dim3(mla::kLdsProbeThreads), 0,
+                       stream, iters, sink, clk);
+  else
+    hipLaunchKernelGGL(mla::probe_lds_kernel<1>, dim3(blocks), dim3(mla::kLdsProbeThreads), 0,
+                       stream, iters, sink, clk);
+  return hipGetLastError();
+}
 
 extern "C" hipError_t mla_launch_probe_stream_read(const void* src, size_t bytes, unsigned* sink,
                                                    int blocks, hipStream_t stream) {
