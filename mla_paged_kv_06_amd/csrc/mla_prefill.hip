@@ -200,24 +200,41 @@ __global__ void __launch_bounds__(pf::kThreads, 1) prefill_attention_kernel(cons
                                                                   0, 0, 0);
         }
       }
-      // ---- masks and row maxima (lane holds keys 16 tt + 4 g + r)
+      // ---- masks and row maxima (lane holds keys 16 tt + 4 g + r); a block
+      //      every key of which every row of the wave sees needs no mask
       float x[2][16];
       float mt[2];
+      const bool whole = k0 + kBK <= kend && (!p.causal || k0 + kBK - 1 <= row_base);
+      if (whole) {
 #pragma unroll
-      for (int rt = 0; rt < 2; ++rt) {
-        const int row = row_base + 16 * rt + l16;
-        mt[rt] = -INFINITY;
+        for (int rt = 0; rt < 2; ++rt) {
 #pragma unroll
-        for (int tt = 0; tt < 4; ++tt) {
+          for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int key = k0 + 16 * tt + 4 * g + r;
-            const bool ok = key < kend && (!p.causal || key <= row);
-            x[rt][4 * tt + r] = ok ? sacc[rt][tt][r] : -INFINITY;
-            mt[rt] = fmaxf(mt[rt], x[rt][4 * tt + r]);
-          }
+            for (int r = 0; r < 4; ++r) x[rt][4 * tt + r] = sacc[rt][tt][r];
+          float m0 = fmaxf(fmaxf(x[rt][0], x[rt][1]), fmaxf(x[rt][2], x[rt][3]));
+          float m1 = fmaxf(fmaxf(x[rt][4], x[rt][5]), fmaxf(x[rt][6], x[rt][7]));
+          float m2 = fmaxf(fmaxf(x[rt][8], x[rt][9]), fmaxf(x[rt][10], x[rt][11]));
+          float m3 = fmaxf(fmaxf(x[rt][12], x[rt][13]), fmaxf(x[rt][14], x[rt][15]));
+          mt[rt] = wave_max_x4(fmaxf(fmaxf(m0, m1), fmaxf(m2, m3)));
         }
-        mt[rt] = wave_max_x4(mt[rt]);
+      } else {
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt) {
+          const int row = row_base + 16 * rt + l16;
+          mt[rt] = -INFINITY;
+#pragma unroll
+          for (int tt = 0; tt < 4; ++tt) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int key = k0 + 16 * tt + 4 * g + r;
+              const bool ok = key < kend && (!p.causal || key <= row);
+              x[rt][4 * tt + r] = ok ? sacc[rt][tt][r] : -INFINITY;
+              mt[rt] = fmaxf(mt[rt], x[rt][4 * tt + r]);
+            }
+          }
+          mt[rt] = wave_max_x4(mt[rt]);
+        }
       }
       // ---- online softmax, one rescale decision for the wave
       const bool grow = (mt[0] - m_used[0]) * sl2 > kRescaleThreshold ||

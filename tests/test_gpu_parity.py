@@ -421,3 +421,66 @@ def test_error_codes(mla):
     assert e.value.status == 3
     with pytest.raises(TypeError):
         mla.decode_paged(q.float(), kv, bt, sl, 0.1, False, meta, splits)
+
+
+# ---------------------------------------------------------------- HIP graphs
+def _graph_replays_match(mla, case, step, replays=3):
+    """Capture `step` (which writes fresh outputs it returns) in a HIP graph,
+    replay it several times with eager work and host synchronisation in
+    between, and compare every replay with the eager result bit for bit."""
+    out0, lse0 = step()
+    torch.cuda.synchronize()
+    ref_o = out0.view(torch.int16).clone()
+    ref_l = lse0.clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        out_g, lse_g = step()
+    torch.cuda.synchronize()
+    for r in range(replays):
+        step()  # eager work between replays (the same step, launched eagerly)
+        torch.cuda.synchronize()
+        out_g.fill_(-3.0)  # only the replay can restore the outputs
+        lse_g.fill_(-3.0)
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out_g.view(torch.int16), ref_o), f"out, replay {r}"
+        assert torch.equal(lse_g, ref_l), f"lse, replay {r}"
+
+
+@pytest.mark.parametrize("L,s_q,h_q", [([3000, 129, 64, 0, 700], 1, 16), ([5000, 70, 2100], 2, 128),
+                                       ([40] * 1100, 1, 16)])
+def test_graph_replays_equal_eager(mla, L, s_q, h_q):
+    """Whole decode steps (schedule, decode, combine) captured in a HIP graph
+    give the eager bits on every replay: no memset nodes, nothing left over
+    between replays."""
+    _say(f"[graph] L={L[:3]} s_q={s_q} h_q={h_q}")
+    case = make_case(L, s_q, h_q, s_q > 1, seed=211 + h_q, pool_factor=1.25, poison_unused=True,
+                     poison_tail=True)
+    q, kv, bt, sl = to_dev(case)
+    b = case.batch
+    out = torch.empty((b, s_q, h_q, 512), dtype=torch.bfloat16, device="cuda:0")
+    lse = torch.empty((b, s_q, h_q), dtype=torch.float32, device="cuda:0")
+    fused = mla.prefers_in_decode(b, s_q, h_q, case.max_pages)
+    ws = torch.empty((mla.workspace_bytes(b, s_q, h_q),), dtype=torch.uint8, device="cuda:0")
+    splits = torch.empty((b + 1,), dtype=torch.int32, device="cuda:0")
+    meta = torch.empty((mla.num_partitions(s_q, h_q), mla.META_INTS), dtype=torch.int32,
+                       device="cuda:0")
+    lib = mla.load_library()
+
+    def step():
+        st = torch.cuda.current_stream()
+        if not fused:
+            mla._check("mla_get_metadata", lib.mla_get_metadata(
+                mla._ptr(sl), b, s_q, h_q, 0, mla._ptr(meta), mla._ptr(splits), mla._stream(st)))
+        mla.decode_paged(q, kv, bt, sl, case.softmax_scale, case.causal,
+                         None if fused else meta, splits, workspace=ws, out=out, lse=lse,
+                         stream=st)
+        mla.combine(ws, splits, b, s_q, h_q, out, lse, stream=st)
+        return out, lse
+
+    _graph_replays_match(mla, case, step)
+    o, l = out.view(torch.int16).cpu().numpy().view(np.uint16), lse.cpu().numpy()
+    ref_out, ref_lse = oracle.decode_ref(case, batches=[0, 1])
+    compare(oracle.bf16_to_f64(o), l.astype(np.float64), ref_out, ref_lse, batches=[0, 1])

@@ -99,3 +99,34 @@ def test_noalloc_refuses_shapes_beyond_its_scratch(mla):
     assert st == 0
     assert torch.equal(out.view(torch.int16), ref_out.view(torch.int16))
     assert torch.equal(lse, ref_lse)
+
+
+def test_noalloc_in_a_graph(mla):
+    """The no-allocation step captured in a HIP graph (its purpose): every
+    replay, with eager work in between, gives the eager bits."""
+    case = make_case([3000, 129, 64, 0, 700], 2, 64, True, seed=351, pool_factor=1.25,
+                     poison_unused=True, poison_tail=True)
+    q, kv, bt, sl = _dev(case)
+    out = torch.empty((case.batch, 2, 64, 512), dtype=torch.bfloat16, device="cuda:0")
+    lse = torch.empty((case.batch, 2, 64), dtype=torch.float32, device="cuda:0")
+    mla.decode_step_noalloc(q, kv, bt, sl, case.softmax_scale, True, out, lse)
+    torch.cuda.synchronize()
+    ref_o, ref_l = out.view(torch.int16).clone(), lse.clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        mla.decode_step_noalloc(q, kv, bt, sl, case.softmax_scale, True, out, lse)
+    torch.cuda.synchronize()
+    for r in range(3):
+        out.fill_(-3.0)
+        lse.fill_(-3.0)
+        small = make_case([100, 3], 1, 16, False, seed=352 + r)
+        ts = _dev(small)
+        st, _, _ = _noalloc(mla, small, ts)  # another call on the same scratch
+        assert st == 0
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), ref_o), f"out, replay {r}"
+        assert torch.equal(lse, ref_l), f"lse, replay {r}"
