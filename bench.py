@@ -834,6 +834,31 @@ def machine_limits(mla, dev):
             if it:
                 per_clk.append(4000 * 16 * 512 * nbytes_lane / float(clk.cpu().numpy()[0]))
         lds[name] = round(float(np.median(per_clk)), 1)
+    # matrix work in one wave of each SIMD beside vector work in the other:
+    # launch time together against each alone (1.0 of the sum: no overlap)
+    isink = torch.empty(256 * 512, dtype=torch.float32, device=dev)
+    iclk = torch.zeros(2, dtype=torch.int64, device=dev)
+    t_kind = {}
+    for kind in range(5):
+        ts = []
+        for it in range(3):
+            e0.record()
+            rc = lib.mla_probe_issue(kind, 20000, 256, ctypes.c_void_p(isink.data_ptr()),
+                                     ctypes.c_void_p(iclk.data_ptr()), st())
+            e1.record()
+            torch.cuda.synchronize()
+            if rc:
+                raise RuntimeError(f"probe status {rc}")
+            if it:
+                ts.append(e0.elapsed_time(e1) * 1e3)
+        t_kind[kind] = float(np.median(ts))
+    issue = {"us_mfma_alone": round(t_kind[0], 1), "us_fma_alone": round(t_kind[1], 1),
+             "us_exp_alone": round(t_kind[2], 1), "us_mfma_with_fma": round(t_kind[3], 1),
+             "us_mfma_with_exp": round(t_kind[4], 1),
+             "fma_together_over_sum": round(t_kind[3] / (t_kind[0] + t_kind[1]), 3),
+             "exp_together_over_sum": round(t_kind[4] / (t_kind[0] + t_kind[2]), 3),
+             "work": "256 workgroups x 8 waves, 20000 trips: waves 0-3 4 bf16 16x16x32 MFMA a "
+                     "trip, waves 4-7 16 fp32 FMA or 4 v_exp_f32 a trip"}
     torch.cuda.empty_cache()
     return {"stream_read_GB_per_s": round(read_gbs, 1),
             "stream_read_frac_of_spec": round(read_gbs / HBM_PEAK_GBS, 4),
@@ -842,7 +867,8 @@ def machine_limits(mla, dev):
             "mfma_loop_frac_of_spec": round(mfma_tf / BF16_PEAK_TFLOPS, 4),
             "shader_clock_GHz_under_mfma": round(float(np.median(ghz)), 3),
             "spec_clock_GHz": 2.4,
-            "lds_read_bytes_per_clock_per_cu": lds}
+            "lds_read_bytes_per_clock_per_cu": lds,
+            "matrix_beside_vector_work": issue}
 
 
 def trace_stats(path):

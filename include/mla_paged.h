@@ -395,6 +395,18 @@ mla_status_t mla_probe_mfma(int32_t iters, int32_t blocks, void* sink, void* clo
  * 8-byte count), so bytes per clock per compute unit follow. */
 mla_status_t mla_probe_lds(int32_t kind, int32_t iters, int32_t blocks, void* sink, void* clocks,
                            hipStream_t stream);
+/* mla_probe_issue: whether matrix and vector work share a SIMD's time.  In
+ * each of `blocks` workgroups of 8 waves (waves w and w + 4 on one SIMD),
+ * kind 0: waves 0-3 run `iters` x 4 independent bf16 16x16x32 matrix
+ * instructions, waves 4-7 nothing; kind 1: waves 4-7 run `iters` x 16
+ * independent fp32 fused multiply-adds, waves 0-3 nothing; kind 2: waves 4-7
+ * run `iters` x 4 independent exponentials; kind 3: kinds 0 and 1 at once;
+ * kind 4: kinds 0 and 2 at once.  Writes blocks * 512 floats to `sink` and
+ * workgroup 0's shader-clock cycles of waves 0 and 4 to `clocks` (two 8-byte
+ * counts, device).  A launch of kind 3 that takes as long as kinds 0 and 1
+ * back to back means the two kinds of work do not overlap. */
+mla_status_t mla_probe_issue(int32_t kind, int32_t iters, int32_t blocks, void* sink,
+                             void* clocks, hipStream_t stream);
 
 /* Static, human-readable text of a status code. */
 const char* mla_status_string(mla_status_t status);

@@ -19,6 +19,8 @@ extern "C" hipError_t mla_launch_check_contents(const int32_t* seqlens, const in
                                                 hipStream_t stream);
 extern "C" hipError_t mla_launch_probe_stream_read(const void* src, size_t bytes, unsigned* sink,
                                                    int blocks, hipStream_t stream);
+extern "C" hipError_t mla_launch_probe_issue(int kind, int iters, int blocks, float* sink,
+                                             unsigned long long* clk, hipStream_t stream);
 extern "C" hipError_t mla_launch_probe_lds(int kind, int iters, int blocks, int* sink,
                                            unsigned long long* clk, hipStream_t stream);
 extern "C" hipError_t mla_launch_probe_mfma(int iters, int blocks, float* sink,
@@ -444,6 +446,16 @@ mla_status_t mla_probe_lds(int32_t kind, int32_t iters, int32_t blocks, void* si
     return MLA_ERR_INVALID_ARGUMENT;
   return mla_launch_probe_lds(kind, iters, blocks, (int*)sink, (unsigned long long*)clocks,
                               stream) == hipSuccess
+             ? MLA_OK
+             : MLA_ERR_HIP;
+}
+
+mla_status_t mla_probe_issue(int32_t kind, int32_t iters, int32_t blocks, void* sink,
+                             void* clocks, hipStream_t stream) {
+  if (!sink || !clocks || iters <= 0 || blocks <= 0 || kind < 0 || kind > 4)
+    return MLA_ERR_INVALID_ARGUMENT;
+  return mla_launch_probe_issue(kind, iters, blocks, (float*)sink, (unsigned long long*)clocks,
+                                stream) == hipSuccess
              ? MLA_OK
              : MLA_ERR_HIP;
 }

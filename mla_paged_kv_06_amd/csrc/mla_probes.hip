@@ -7,7 +7,10 @@
 //     the shader clock against the constant 100 MHz real-time counter;
 //   - LDS reads of the two kinds the decode issues: 16-byte reads of key
 //     fragments (rows 1152 bytes apart, XOR-swizzled chunks) and transposed
-//     8-byte reads of value fragments, 8 waves per compute unit.
+//     8-byte reads of value fragments, 8 waves per compute unit;
+//   - matrix instructions in one wave of a SIMD beside plain vector work
+//     (fused multiply-adds or exponentials) in the other, and each alone:
+//     whether the two kinds of work share a SIMD's time or overlap.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -142,7 +145,81 @@ __global__ void __launch_bounds__(kLdsProbeThreads)
   sink[(size_t)blockIdx.x * kLdsProbeThreads + tid] = (int)(acc.x ^ acc.y ^ acc.z ^ acc.w);
 }
 
+constexpr int kIssueThreads = 512;  // waves w and w + 4 share a SIMD
+
+// kind 0: waves 0-3 run iters x 4 independent bf16 16x16x32 matrix
+// instructions, waves 4-7 nothing; kind 1: waves 4-7 run iters x 16
+// independent fused multiply-adds, waves 0-3 nothing; kind 2: waves 4-7 run
+// iters x 4 independent exponentials (v_exp_f32); kind 3 = kinds 0 and 1
+// together, kind 4 = kinds 0 and 2 together.  Workgroup 0 records the
+// shader-clock cycles of the loops of wave 0 (clk[0]) and wave 4 (clk[1]).
+template <int kKind>
+__global__ void __launch_bounds__(kIssueThreads)
+    probe_issue_kernel(int iters, float* __restrict__ sink, unsigned long long* __restrict__ clk) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  constexpr bool kMat = kKind == 0 || kKind == 3 || kKind == 4;
+  constexpr bool kFma = kKind == 1 || kKind == 3;
+  constexpr bool kExp = kKind == 2 || kKind == 4;
+  pbf16x8 a, b;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    a[k] = (__bf16)(0.001f * (float)(lane + k));
+    b[k] = (__bf16)(0.002f * (float)(lane - k));
+  }
+  pf32x4 c[kMfmaChains];
+#pragma unroll
+  for (int k = 0; k < kMfmaChains; ++k) c[k] = pf32x4{0.f, 0.f, 0.f, 0.f};
+  float x[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) x[i] = 0.5f + 0.001f * (float)(lane + i);
+  unsigned long long t0 = 0;
+  const bool stamp = blockIdx.x == 0 && (tid == 0 || tid == 256);
+  if (stamp) t0 = __builtin_readcyclecounter();
+  if (wave < 4) {
+    if (kMat) {
+      for (int it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int k = 0; k < kMfmaChains; ++k)
+          c[k] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c[k], 0, 0, 0);
+      }
+    }
+  } else if (kFma) {
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+      for (int r = 0; r < 2; ++r)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) x[i] = __builtin_fmaf(x[i], 0.999f, 0.0001f);
+    }
+  } else if (kExp) {
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) x[i] = __builtin_amdgcn_exp2f(-x[i]);
+    }
+  }
+  if (stamp) clk[tid == 0 ? 0 : 1] = __builtin_readcyclecounter() - t0;
+  float s = 0.f;
+#pragma unroll
+  for (int k = 0; k < kMfmaChains; ++k) s += c[k][0] + c[k][1] + c[k][2] + c[k][3];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) s += x[i];
+  sink[(size_t)blockIdx.x * kIssueThreads + tid] = s;
+}
+
 }  // namespace mla
+
+extern "C" hipError_t mla_launch_probe_issue(int kind, int iters, int blocks, float* sink,
+                                             unsigned long long* clk, hipStream_t stream) {
+  const dim3 grid(blocks), block(mla::kIssueThreads);
+  switch (kind) {
+    case 0: hipLaunchKernelGGL(mla::probe_issue_kernel<0>, grid, block, 0, stream, iters, sink, clk); break;
+    case 1: hipLaunchKernelGGL(mla::probe_issue_kernel<1>, grid, block, 0, stream, iters, sink, clk); break;
+    case 2: hipLaunchKernelGGL(mla::probe_issue_kernel<2>, grid, block, 0, stream, iters, sink, clk); break;
+    case 3: hipLaunchKernelGGL(mla::probe_issue_kernel<3>, grid, block, 0, stream, iters, sink, clk); break;
+    default: hipLaunchKernelGGL(mla::probe_issue_kernel<4>, grid, block, 0, stream, iters, sink, clk); break;
+  }
+  return hipGetLastError();
+}
 
 extern "C" hipError_t mla_launch_probe_lds(int kind, int iters, int blocks, int* sink,
                                            unsigned long long* clk, hipStream_t stream) {
