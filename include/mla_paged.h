@@ -333,11 +333,12 @@ mla_status_t mla_decode_paged_fp8(const void* q, const void* kv_fp8, const int32
  * mla_prefill_expand_kv widens the latents:
  *   latent  bf16 [tokens][latent_stride]: c_t = latent[t][0:512] (a cache
  *           entry [c ; r] has latent_stride 576); latent_stride >= 512, a
- *           multiple of 8
+ *           multiple of 8, at most 2^21 (else MLA_ERR_UNSUPPORTED)
  *   w_uk, w_uv  bf16 [h_q][128][512]: W_UK,h and W_UV,h as stored
  *   k_nope  bf16 [tokens][h_q][128]: k_nope[t][h] = W_UK,h c_t
  *   v       bf16 [tokens][h_q][128]: v[t][h] = W_UV,h c_t
- * fp32 accumulation, one rounding to bf16 (nearest even).  Two launches.
+ * fp32 accumulation, one rounding to bf16 (nearest even).  One launch: both
+ * products as [tokens][512] x [512][h_q * 128] matrix products.
  *
  * mla_prefill_attention: packed prompts, prompt s holding tokens
  * cu_seqlens[s] .. cu_seqlens[s+1] - 1 (cu_seqlens int32 [batch + 1],

@@ -31,6 +31,10 @@
 
 #include "mla_device.h"
 
+// the LDS-DMA copies write M0 in inline assembly (no compiled code of the
+// expansion kernel uses M0)
+#pragma clang diagnostic ignored "-Winline-asm"
+
 namespace mla {
 
 constexpr int kNope = 128;       // per-head query part and value head width
@@ -175,6 +179,138 @@ __global__ void __launch_bounds__(256, 2) absorb_kernel(const uint16_t* __restri
   }
 }
 
+// Prefill expansion as one matrix product per weight:
+//   C[t][n] = sum_k latent[t][k] W[n][k],  n = 128 h + d,  k < 512,
+// k_nope (W_UK) and v (W_UV) both [T][H][128] = [T][N].  A workgroup of 8
+// waves owns a 256 x 256 tile of C (wave w: rows 64 (w & 3) .., columns
+// 128 (w >> 2) ..; 4 x 8 MFMA 16x16x32 tiles, 128 accumulators).  The
+// contraction runs in 16 stages of 32 values; each stage's 256 x 32 slices
+// of the latents and of W (16 KiB each) are copied HBM -> LDS by LDS-DMA
+// (buffer_load ... lds, four 1 KiB copies per wave) into a ring of four
+// buffers, three stages ahead.  LDS rows are 64 bytes; the 16-byte chunk c
+// of row r sits at c ^ ((r >> 1) & 3), so the rows one fragment read
+// touches fall on distinct banks.  Buffer resources bounded at the last
+// row (T, N) make rows past the ends read as zero.
+namespace ex {
+constexpr int kBM = 256, kBN = 256, kBK = 32;
+constexpr int kStages = kDv / kBK;  // 16
+constexpr int kRing = 4;
+constexpr int kSliceB = kBM * kBK * 2;  // 16 KiB
+constexpr int kThreads = 512;
+}  // namespace ex
+
+__device__ __forceinline__ void ex_copy16(MLA_LDS char* lds, int voff, i32x4 rsrc, int soff) {
+  const int m0 = __builtin_amdgcn_readfirstlane((int)(size_t)lds);
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 4\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               :
+               : "s"(m0), "v"(voff), "s"(rsrc), "s"(soff)
+               : "memory", "m0");
+}
+
+__device__ __forceinline__ i32x4 ex_rsrc(const void* base, int bytes) {
+  const unsigned long long a = (unsigned long long)base;
+  return i32x4{__builtin_amdgcn_readfirstlane((int)(unsigned)a),
+               __builtin_amdgcn_readfirstlane((int)((a >> 32) & 0xFFFF)),
+               __builtin_amdgcn_readfirstlane(bytes), kBufferFlags};
+}
+
+template <int kImm>
+__device__ __forceinline__ void ex_wait() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(kImm);
+  asm volatile("" ::: "memory");
+}
+
+__global__ void __launch_bounds__(ex::kThreads, 1)
+    expand_gemm_kernel(const uint16_t* __restrict__ latent, int latent_stride, int T,
+                       const uint16_t* __restrict__ w0, const uint16_t* __restrict__ w1, int N,
+                       uint16_t* __restrict__ out0, uint16_t* __restrict__ out1) {
+  using namespace ex;
+  __shared__ __attribute__((aligned(1024))) char ring_[kRing * 2 * kSliceB];
+  MLA_LDS char* ring = (MLA_LDS char*)ring_;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l16 = lane & 15, g = lane >> 4;
+  const int m0 = blockIdx.x * kBM;
+  const int n0 = blockIdx.y * kBN;
+  const uint16_t* w = blockIdx.z ? w1 : w0;
+  uint16_t* out = blockIdx.z ? out1 : out0;
+  const int rows_a = min(kBM, T - m0), rows_b = min(kBN, N - n0);
+  const i32x4 ra = ex_rsrc(latent + (size_t)m0 * latent_stride, rows_a * latent_stride * 2);
+  const i32x4 rb = ex_rsrc(w + (size_t)n0 * kDv, rows_b * kDv * 2);
+  // this wave's copies of a stage: slices 2 w and 2 w + 1 of A and of B
+  // (copy i, lane l: row 16 i + l / 4, physical chunk l & 3)
+  int va[2], vb[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int row = 16 * (2 * wave + u) + (lane >> 2);
+    const int lc = (lane & 3) ^ ((row >> 1) & 3);
+    va[u] = row * latent_stride * 2 + 16 * lc;
+    vb[u] = row * kDv * 2 + 16 * lc;
+  }
+  auto issue = [&](int st) __attribute__((always_inline)) {
+    MLA_LDS char* buf = ring + (st & (kRing - 1)) * 2 * kSliceB;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      ex_copy16(buf + 1024 * (2 * wave + u), va[u], ra, st * kBK * 2);
+      ex_copy16(buf + kSliceB + 1024 * (2 * wave + u), vb[u], rb, st * kBK * 2);
+    }
+  };
+  // fragment rows: A row 64 (w & 3) + 16 mt + l16, B row 128 (w >> 2) + 16 nt + l16
+  const int phys = g ^ ((l16 >> 1) & 3);
+  const int fa = (64 * (wave & 3) + l16) * 64 + 16 * phys;
+  const int fb = kSliceB + (128 * (wave >> 2) + l16) * 64 + 16 * phys;
+
+  f32x4 acc[8][4];
+#pragma unroll
+  for (int nt = 0; nt < 8; ++nt)
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) acc[nt][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  issue(0);
+  issue(1);
+  issue(2);
+  for (int st = 0; st < kStages; ++st) {
+    // this wave's copies of stage st landed (the two later stages may fly)
+    if (st + 2 < kStages)
+      ex_wait<0x0F70 | 8>();
+    else if (st + 1 < kStages)
+      ex_wait<0x0F70 | 4>();
+    else
+      ex_wait<0x0F70>();
+    __builtin_amdgcn_s_barrier();  // every wave's copies landed; stage st - 1 read
+    asm volatile("" ::: "memory");
+    if (st + 3 < kStages) issue(st + 3);
+    const MLA_LDS char* buf = ring + (st & (kRing - 1)) * 2 * kSliceB;
+    bf16x8 af[4], bf[8];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) af[mt] = *(const MLA_LDS bf16x8*)(buf + fa + 1024 * mt);
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt) bf[nt] = *(const MLA_LDS bf16x8*)(buf + fb + 1024 * nt);
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt)
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+        acc[nt][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf[nt], af[mt], acc[nt][mt], 0, 0, 0);
+  }
+  // lane (g, l16) holds columns 4 g .. 4 g + 3 of each 16-column tile, row l16
+  const int ncol = n0 + 128 * (wave >> 2);
+  if (ncol >= N) return;
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) {
+    const int m = m0 + 64 * (wave & 3) + 16 * mt + l16;
+    if (m < T) {
+      uint16_t* o = out + (size_t)m * N + ncol + 4 * g;
+#pragma unroll
+      for (int nt = 0; nt < 8; ++nt) {
+        const bf16x2 a = to_bf16x2(acc[nt][mt][0], acc[nt][mt][1]);
+        const bf16x2 b = to_bf16x2(acc[nt][mt][2], acc[nt][mt][3]);
+        *(bf16x4*)(o + 16 * nt) = bf16x4{a[0], a[1], b[0], b[1]};
+      }
+    }
+  }
+}
+
 // tiles in flight ahead of the one computed, per wave (registers: rows
 // 4 KS (D + 1)); a workgroup's 16 tiles are 4 per wave.  Two workgroups fit
 // a CU (registers and 2 x 68 KiB of LDS).
@@ -215,13 +351,9 @@ extern "C" hipError_t mla_launch_prefill_expand(const uint16_t* latent, int late
                                                 const uint16_t* w_uk, const uint16_t* w_uv, int H,
                                                 uint16_t* k_nope, uint16_t* v, hipStream_t stream) {
   using namespace mla;
-  const dim3 grid((T + kRowChunk - 1) / kRowChunk, kNope / 64, H);
-  hipLaunchKernelGGL((absorb_kernel<kDv, 64, kOutputDepth>), grid, dim3(256), 0, stream, latent,
-                     latent_stride, 0, w_uk, k_nope, kNope, T, H, kNope, (const uint16_t*)nullptr,
-                     0);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((absorb_kernel<kDv, 64, kOutputDepth>), grid, dim3(256), 0, stream, latent,
-                     latent_stride, 0, w_uv, v, kNope, T, H, kNope, (const uint16_t*)nullptr, 0);
+  const int N = H * kNope;
+  const dim3 grid((T + ex::kBM - 1) / ex::kBM, (N + ex::kBN - 1) / ex::kBN, 2);
+  hipLaunchKernelGGL(expand_gemm_kernel, grid, dim3(ex::kThreads), 0, stream, latent,
+                     latent_stride, T, w_uk, w_uv, N, k_nope, v);
   return hipGetLastError();
 }

@@ -380,6 +380,8 @@ mla_status_t mla_prefill_expand_kv(const void* latent, int32_t latent_stride, in
   if (!latent || !w_uk || !w_uv || !k_nope || !v) return MLA_ERR_INVALID_ARGUMENT;
   if (tokens <= 0 || h_q <= 0 || latent_stride < MLA_V_DIM || (latent_stride & 7))
     return MLA_ERR_INVALID_ARGUMENT;
+  // 256 latent rows stay addressable by 32-bit byte offsets
+  if (latent_stride > (1 << 21)) return MLA_ERR_UNSUPPORTED;
   if (((uintptr_t)latent | (uintptr_t)w_uk | (uintptr_t)w_uv | (uintptr_t)k_nope |
        (uintptr_t)v) & 15)
     return MLA_ERR_INVALID_ARGUMENT;

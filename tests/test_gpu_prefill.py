@@ -73,6 +73,7 @@ SHAPES = [
     ([700], 16, True),
     ([700, 129], 16, False),
     ([513, 0, 1000], 8, True),
+    ([300, 45], 3, True),  # odd head count: the expansion's last column tile is half empty
 ]
 
 
