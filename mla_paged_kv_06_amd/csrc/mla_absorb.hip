@@ -324,10 +324,19 @@ extern "C" hipError_t mla_launch_absorb_query(const uint16_t* q_c, const uint16_
                                               const uint16_t* w_uk_t, int M, int H,
                                               uint16_t* q_out, hipStream_t stream) {
   using namespace mla;
-  // 256 columns (a 64 KiB slice of W) per workgroup
-  const dim3 grid((M + kRowChunk - 1) / kRowChunk, kDv / 256, H);
-  hipLaunchKernelGGL((absorb_kernel<kNope, 256, kQueryDepth>), grid, dim3(256), 0, stream, q_c,
-                     H * kNope, kNope, w_uk_t, q_out, kD, M, H, kDv, q_r, kRope);
+  // 256 columns (a 64 KiB slice of W) per workgroup; with fewer workgroups
+  // than compute units that way (decode-size batches), 128 columns, so that
+  // twice as many CUs stream the weights
+  const int chunks = (M + kRowChunk - 1) / kRowChunk;
+  if ((long long)chunks * (kDv / 256) * H < 256) {
+    const dim3 grid(chunks, kDv / 128, H);
+    hipLaunchKernelGGL((absorb_kernel<kNope, 128, kQueryDepth>), grid, dim3(256), 0, stream,
+                       q_c, H * kNope, kNope, w_uk_t, q_out, kD, M, H, kDv, q_r, kRope);
+  } else {
+    const dim3 grid(chunks, kDv / 256, H);
+    hipLaunchKernelGGL((absorb_kernel<kNope, 256, kQueryDepth>), grid, dim3(256), 0, stream,
+                       q_c, H * kNope, kNope, w_uk_t, q_out, kD, M, H, kDv, q_r, kRope);
+  }
   return hipGetLastError();
 }
 
@@ -335,10 +344,20 @@ extern "C" hipError_t mla_launch_absorb_query(const uint16_t* q_c, const uint16_
 extern "C" hipError_t mla_launch_absorb_output(const uint16_t* lat_out, const uint16_t* w_uv,
                                                int M, int H, uint16_t* o, hipStream_t stream) {
   using namespace mla;
-  // 64 columns (a 64 KiB slice of W) per workgroup
-  const dim3 grid((M + kRowChunk - 1) / kRowChunk, kNope / 64, H);
-  hipLaunchKernelGGL((absorb_kernel<kDv, 64, kOutputDepth>), grid, dim3(256), 0, stream, lat_out,
-                     H * kDv, kDv, w_uv, o, kNope, M, H, kNope, (const uint16_t*)nullptr, 0);
+  // 64 columns (a 64 KiB slice of W) per workgroup, 32 for decode-size
+  // batches (as for the query product)
+  const int chunks = (M + kRowChunk - 1) / kRowChunk;
+  if ((long long)chunks * (kNope / 64) * H < 256) {
+    const dim3 grid(chunks, kNope / 32, H);
+    hipLaunchKernelGGL((absorb_kernel<kDv, 32, kOutputDepth>), grid, dim3(256), 0, stream,
+                       lat_out, H * kDv, kDv, w_uv, o, kNope, M, H, kNope,
+                       (const uint16_t*)nullptr, 0);
+  } else {
+    const dim3 grid(chunks, kNope / 64, H);
+    hipLaunchKernelGGL((absorb_kernel<kDv, 64, kOutputDepth>), grid, dim3(256), 0, stream,
+                       lat_out, H * kDv, kDv, w_uv, o, kNope, M, H, kNope,
+                       (const uint16_t*)nullptr, 0);
+  }
   return hipGetLastError();
 }
 
