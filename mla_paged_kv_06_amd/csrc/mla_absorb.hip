@@ -184,18 +184,19 @@ __global__ void __launch_bounds__(256, 2) absorb_kernel(const uint16_t* __restri
 // k_nope (W_UK) and v (W_UV) both [T][H][128] = [T][N].  A workgroup of 8
 // waves owns a 256 x 256 tile of C (wave w: rows 64 (w & 3) .., columns
 // 128 (w >> 2) ..; 4 x 8 MFMA 16x16x32 tiles, 128 accumulators).  The
-// contraction runs in 16 stages of 32 values; each stage's 256 x 32 slices
-// of the latents and of W (16 KiB each) are copied HBM -> LDS by LDS-DMA
-// (buffer_load ... lds, four 1 KiB copies per wave) into a ring of four
-// buffers, three stages ahead.  LDS rows are 64 bytes; the 16-byte chunk c
-// of row r sits at c ^ ((r >> 1) & 3), so the rows one fragment read
-// touches fall on distinct banks.  Buffer resources bounded at the last
-// row (T, N) make rows past the ends read as zero.
+// contraction runs in 8 stages of 64 values (two MFMA k-steps); each
+// stage's 256 x 64 slices of the latents and of W (32 KiB each) are copied
+// HBM -> LDS by LDS-DMA (buffer_load ... lds, eight 1 KiB copies per wave)
+// into the other of two buffers while the current stage computes.  LDS
+// rows are 128 bytes; the 16-byte chunk c of row r sits at c ^ (r & 7), so
+// the rows one fragment read touches fall on distinct banks.  Buffer
+// resources bounded at the last row (T, N) make rows past the ends read as
+// zero.
 namespace ex {
-constexpr int kBM = 256, kBN = 256, kBK = 32;
-constexpr int kStages = kDv / kBK;  // 16
-constexpr int kRing = 4;
-constexpr int kSliceB = kBM * kBK * 2;  // 16 KiB
+constexpr int kBM = 256, kBN = 256, kBK = 64;
+constexpr int kStages = kDv / kBK;  // 8
+constexpr int kRing = 2;
+constexpr int kSliceB = kBM * kBK * 2;  // 32 KiB
 constexpr int kThreads = 512;
 }  // namespace ex
 
@@ -238,28 +239,30 @@ __global__ void __launch_bounds__(ex::kThreads, 1)
   const int rows_a = min(kBM, T - m0), rows_b = min(kBN, N - n0);
   const i32x4 ra = ex_rsrc(latent + (size_t)m0 * latent_stride, rows_a * latent_stride * 2);
   const i32x4 rb = ex_rsrc(w + (size_t)n0 * kDv, rows_b * kDv * 2);
-  // this wave's copies of a stage: slices 2 w and 2 w + 1 of A and of B
-  // (copy i, lane l: row 16 i + l / 4, physical chunk l & 3)
-  int va[2], vb[2];
+  // this wave's copies of a stage: 1 KiB pieces 4 w .. 4 w + 3 of the A and
+  // of the B slice (piece i, lane l: row 8 i + l / 8, physical chunk l & 7)
+  int va[4], vb[4];
 #pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const int row = 16 * (2 * wave + u) + (lane >> 2);
-    const int lc = (lane & 3) ^ ((row >> 1) & 3);
+  for (int u = 0; u < 4; ++u) {
+    const int row = 8 * (4 * wave + u) + (lane >> 3);
+    const int lc = (lane & 7) ^ (row & 7);
     va[u] = row * latent_stride * 2 + 16 * lc;
     vb[u] = row * kDv * 2 + 16 * lc;
   }
   auto issue = [&](int st) __attribute__((always_inline)) {
     MLA_LDS char* buf = ring + (st & (kRing - 1)) * 2 * kSliceB;
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      ex_copy16(buf + 1024 * (2 * wave + u), va[u], ra, st * kBK * 2);
-      ex_copy16(buf + kSliceB + 1024 * (2 * wave + u), vb[u], rb, st * kBK * 2);
+    for (int u = 0; u < 4; ++u) {
+      ex_copy16(buf + 1024 * (4 * wave + u), va[u], ra, st * kBK * 2);
+      ex_copy16(buf + kSliceB + 1024 * (4 * wave + u), vb[u], rb, st * kBK * 2);
     }
   };
-  // fragment rows: A row 64 (w & 3) + 16 mt + l16, B row 128 (w >> 2) + 16 nt + l16
-  const int phys = g ^ ((l16 >> 1) & 3);
-  const int fa = (64 * (wave & 3) + l16) * 64 + 16 * phys;
-  const int fb = kSliceB + (128 * (wave >> 2) + l16) * 64 + 16 * phys;
+  // fragment rows: A row 64 (w & 3) + 16 mt + l16, B row 128 (w >> 2) + 16 nt + l16;
+  // k-step ks of a stage reads logical chunk 4 ks + g of its row
+  const int fa0 = (64 * (wave & 3) + l16) * 128 + 16 * (g ^ (l16 & 7));
+  const int fa1 = (64 * (wave & 3) + l16) * 128 + 16 * ((4 + g) ^ (l16 & 7));
+  const int fb0 = kSliceB + (128 * (wave >> 2) + l16) * 128 + 16 * (g ^ (l16 & 7));
+  const int fb1 = kSliceB + (128 * (wave >> 2) + l16) * 128 + 16 * ((4 + g) ^ (l16 & 7));
 
   f32x4 acc[8][4];
 #pragma unroll
@@ -268,30 +271,28 @@ __global__ void __launch_bounds__(ex::kThreads, 1)
     for (int mt = 0; mt < 4; ++mt) acc[nt][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   issue(0);
-  issue(1);
-  issue(2);
   for (int st = 0; st < kStages; ++st) {
-    // this wave's copies of stage st landed (the two later stages may fly)
-    if (st + 2 < kStages)
-      ex_wait<0x0F70 | 8>();
-    else if (st + 1 < kStages)
-      ex_wait<0x0F70 | 4>();
-    else
-      ex_wait<0x0F70>();
+    ex_wait<0x0F70>();             // this wave's copies of stage st landed
     __builtin_amdgcn_s_barrier();  // every wave's copies landed; stage st - 1 read
     asm volatile("" ::: "memory");
-    if (st + 3 < kStages) issue(st + 3);
+    if (st + 1 < kStages) issue(st + 1);
     const MLA_LDS char* buf = ring + (st & (kRing - 1)) * 2 * kSliceB;
-    bf16x8 af[4], bf[8];
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) af[mt] = *(const MLA_LDS bf16x8*)(buf + fa + 1024 * mt);
-#pragma unroll
-    for (int nt = 0; nt < 8; ++nt) bf[nt] = *(const MLA_LDS bf16x8*)(buf + fb + 1024 * nt);
-#pragma unroll
-    for (int nt = 0; nt < 8; ++nt)
+    for (int ks = 0; ks < 2; ++ks) {
+      bf16x8 af[4], bf[8];
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
-        acc[nt][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf[nt], af[mt], acc[nt][mt], 0, 0, 0);
+        af[mt] = *(const MLA_LDS bf16x8*)(buf + (ks ? fa1 : fa0) + 2048 * mt);
+#pragma unroll
+      for (int nt = 0; nt < 8; ++nt)
+        bf[nt] = *(const MLA_LDS bf16x8*)(buf + (ks ? fb1 : fb0) + 2048 * nt);
+#pragma unroll
+      for (int nt = 0; nt < 8; ++nt)
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+          acc[nt][mt] =
+              __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf[nt], af[mt], acc[nt][mt], 0, 0, 0);
+    }
   }
   // lane (g, l16) holds columns 4 g .. 4 g + 3 of each 16-column tile, row l16
   const int ncol = n0 + 128 * (wave >> 2);
