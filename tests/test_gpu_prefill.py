@@ -163,3 +163,33 @@ def test_prefill_errors(mla):
         mla.prefill_attention(_dev(case.q), k_nope, lat[:, 512:], v, cu, 10, 0.0)
     with pytest.raises(mla.MlaError):
         mla.prefill_attention(_dev(case.q), k_nope, lat[:, 512:], v, cu, 10, float("nan"))
+
+
+def test_expansion_rows_are_independent_of_tiling(mla):
+    """Every output value is one fixed-order float32 sum over its latent row
+    and weight row, so a token's k_nope and v do not depend on where its row
+    falls in the 256-row tiles, on how many tokens share the launch, or on
+    the latent row stride: the same bits from 300 tokens at stride 576
+    (cache entries [c ; r]), from their first 37, and from rows 200 .. 299
+    packed at stride 512."""
+    case = make_prefill_case([300], 6, seed=481)
+    lat = _dev(case.latent)                      # [300, 576]
+    wk, wv = _dev(case.w_uk), _dev(case.w_uv)
+    kn_all, v_all = mla.prefill_expand_kv(lat, wk, wv)
+    kn_head, v_head = mla.prefill_expand_kv(lat[:37], wk, wv)
+    packed = lat[200:, :512].contiguous()        # stride 512, rows 200 .. 299
+    kn_tail, v_tail = mla.prefill_expand_kv(packed, wk, wv)
+    torch.cuda.synchronize()
+    bits = lambda t: t.view(torch.int16).cpu()  # noqa: E731
+    assert torch.equal(bits(kn_all[:37]), bits(kn_head))
+    assert torch.equal(bits(v_all[:37]), bits(v_head))
+    assert torch.equal(bits(kn_all[200:]), bits(kn_tail))
+    assert torch.equal(bits(v_all[200:]), bits(v_tail))
+
+
+def test_expansion_refuses_a_huge_latent_stride(mla):
+    case = make_prefill_case([4], 2, seed=491)
+    wk, wv = _dev(case.w_uk), _dev(case.w_uv)
+    big = torch.empty((2, (1 << 21) + 8), dtype=torch.bfloat16, device="cuda:0")
+    with pytest.raises(mla.MlaError):
+        mla.prefill_expand_kv(big, wk, wv)
