@@ -206,3 +206,17 @@ def test_fp8_entry_points_reject_bad_arguments(lib):
     assert lib.mla_decode_paged_fp8(*bad) == 2
     bad = list(args); bad[1] = null
     assert lib.mla_decode_paged_fp8(*bad) == 1
+
+
+def test_probe_arguments_are_checked_on_the_host(lib):
+    """The probes refuse bad arguments before any HIP call."""
+    vp = ctypes.c_void_p
+    lib.mla_probe_issue.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, vp, vp, vp]
+    lib.mla_probe_issue.restype = ctypes.c_int32
+    dummy = vp(16)  # never dereferenced: the checks fail first
+    assert lib.mla_probe_issue(5, 10, 1, dummy, dummy, None) == 1   # no such kind
+    assert lib.mla_probe_issue(-1, 10, 1, dummy, dummy, None) == 1
+    assert lib.mla_probe_issue(0, 0, 1, dummy, dummy, None) == 1    # no trips
+    assert lib.mla_probe_issue(0, 10, 0, dummy, dummy, None) == 1   # no workgroups
+    assert lib.mla_probe_issue(0, 10, 1, None, dummy, None) == 1    # no sink
+    assert lib.mla_probe_issue(0, 10, 1, dummy, None, None) == 1    # no clocks
