@@ -436,28 +436,32 @@ __global__ void __launch_bounds__(sv::kThreadsSV, 1)
         const int row = row0 + 16 * r2 + l16;
         const float lr = stat_l[16 * r2 + l16];
         const float inv = lr > 0.f ? 1.f / lr : 0.f;
-        if (row < prm.R) {
-          if (direct) {
-            uint16_t* orow = out_ptr + ((size_t)b * prm.R + row) * kDv + col_base + 4 * g;
-            static_for<0, kCT>([&](auto cc) __attribute__((always_inline)) {
-              constexpr int ct = decltype(cc)::value;
-              const f32x4 v = o[r2][ct] * inv;
-              const bf16x2 a = to_bf16x2(v[0], v[1]);
-              const bf16x2 d = to_bf16x2(v[2], v[3]);
-              *(bf16x4*)(orow + 16 * ct) = bf16x4{a[0], a[1], d[0], d[1]};
-            });
-          } else {
-            // the normalized partial, rounded to bf16 like the output
-            uint16_t* orow = o_acc + ((size_t)slot * prm.R + row) * kDv + col_base + 4 * g;
-            static_for<0, kCT>([&](auto cc) __attribute__((always_inline)) {
-              constexpr int ct = decltype(cc)::value;
-              const f32x4 v = o[r2][ct] * inv;
-              const bf16x2 a = to_bf16x2(v[0], v[1]);
-              const bf16x2 d = to_bf16x2(v[2], v[3]);
-              *(bf16x4*)(orow + 16 * ct) = bf16x4{a[0], a[1], d[0], d[1]};
-            });
+        // tiles 2 p and 2 p + 1 of this row: a lane swap between 16-lane
+        // groups leaves lane group g with 8 consecutive columns, 16 (2 p + (g
+        // & 1)) + 8 (g >> 1) .. + 7, so each store covers 64 contiguous bytes
+        // of a row
+        uint16_t* orow = direct ? out_ptr + ((size_t)b * prm.R + row) * kDv + col_base
+                                : o_acc + ((size_t)slot * prm.R + row) * kDv + col_base;
+        typedef __attribute__((ext_vector_type(2))) unsigned u32x2;
+        static_for<0, kCT / 2>([&](auto pc) __attribute__((always_inline)) {
+          constexpr int pp = decltype(pc)::value;
+          const f32x4 v0 = o[r2][2 * pp] * inv;
+          const f32x4 v1 = o[r2][2 * pp + 1] * inv;
+          const u32x2 x0 = __builtin_bit_cast(u32x2, bf16x4{to_bf16x2(v0[0], v0[1])[0],
+                                                            to_bf16x2(v0[0], v0[1])[1],
+                                                            to_bf16x2(v0[2], v0[3])[0],
+                                                            to_bf16x2(v0[2], v0[3])[1]});
+          const u32x2 x1 = __builtin_bit_cast(u32x2, bf16x4{to_bf16x2(v1[0], v1[1])[0],
+                                                            to_bf16x2(v1[0], v1[1])[1],
+                                                            to_bf16x2(v1[2], v1[3])[0],
+                                                            to_bf16x2(v1[2], v1[3])[1]});
+          const u32x2 s0 = __builtin_amdgcn_permlane16_swap(x0[0], x1[0], false, false);
+          const u32x2 s1 = __builtin_amdgcn_permlane16_swap(x0[1], x1[1], false, false);
+          if (row < prm.R) {
+            const int col = 16 * (2 * pp + (g & 1)) + 8 * (g >> 1);
+            *(i32x4*)(orow + col) = i32x4{(int)s0[0], (int)s1[0], (int)s0[1], (int)s1[1]};
           }
-        }
+        });
         static_for<0, kCT>([&](auto cc) __attribute__((always_inline)) {
           o[r2][decltype(cc)::value] = f32x4{0.f, 0.f, 0.f, 0.f};
         });
