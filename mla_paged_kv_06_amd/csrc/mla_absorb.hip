@@ -109,19 +109,34 @@ __global__ void __launch_bounds__(256, 2) absorb_kernel(const uint16_t* __restri
     asm volatile("" : "+v"(wo));
     uint16_t* o = out + ((size_t)m * H + h) * out_stride + n0 + 4 * g;
     const bool live = full || m < m_end;
+    typedef __attribute__((ext_vector_type(2))) unsigned u32x2;
 #pragma unroll
-    for (int ct = 0; ct < CT; ++ct) {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int cp = 0; cp < CT / 2; ++cp) {
+      f32x4 acc[2];
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const bf16x8 wf = *(const bf16x8*)(wl + wo + 16 * ct * kRowB + 64 * ks);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf, af[ks], acc, 0, 0, 0);
+      for (int e = 0; e < 2; ++e) {
+        acc[e] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          const bf16x8 wf = *(const bf16x8*)(wl + wo + 16 * (2 * cp + e) * kRowB + 64 * ks);
+          acc[e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf, af[ks], acc[e], 0, 0, 0);
+        }
       }
-      // lane (g, l16) holds columns n0 + 16 ct + 4 g + r of row m
+      // lane (g, l16) holds columns n0 + 16 ct + 4 g + r of row m for the
+      // tiles ct = 2 cp, 2 cp + 1; a swap between 16-lane groups leaves lane
+      // group g with 8 consecutive columns 16 (2 cp + (g & 1)) + 8 (g >> 1)
+      // .. + 7, so each store writes 64 contiguous bytes of a row
+      const bf16x2 a0 = to_bf16x2(acc[0][0], acc[0][1]), b0 = to_bf16x2(acc[0][2], acc[0][3]);
+      const bf16x2 a1 = to_bf16x2(acc[1][0], acc[1][1]), b1 = to_bf16x2(acc[1][2], acc[1][3]);
+      const u32x2 s0 = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(unsigned, a0),
+                                                        __builtin_bit_cast(unsigned, a1), false,
+                                                        false);
+      const u32x2 s1 = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(unsigned, b0),
+                                                        __builtin_bit_cast(unsigned, b1), false,
+                                                        false);
       if (live) {
-        const bf16x2 a = to_bf16x2(acc[0], acc[1]);
-        const bf16x2 b = to_bf16x2(acc[2], acc[3]);
-        *(bf16x4*)(o + 16 * ct) = bf16x4{a[0], a[1], b[0], b[1]};
+        const int col = 16 * (2 * cp + (g & 1)) + 8 * (g >> 1);
+        *(i32x4*)(o - 4 * g + col) = i32x4{(int)s0[0], (int)s1[0], (int)s0[1], (int)s1[1]};
       }
     }
   };
