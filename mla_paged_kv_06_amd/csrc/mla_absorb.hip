@@ -309,20 +309,31 @@ __global__ void __launch_bounds__(ex::kThreads, 1)
               __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf[nt], af[mt], acc[nt][mt], 0, 0, 0);
     }
   }
-  // lane (g, l16) holds columns 4 g .. 4 g + 3 of each 16-column tile, row l16
+  // lane (g, l16) holds columns 4 g .. 4 g + 3 of each 16-column tile, row
+  // l16; a swap between 16-lane groups over tiles 2 p and 2 p + 1 leaves
+  // lane group g with 8 consecutive columns 16 (2 p + (g & 1)) + 8 (g >> 1)
+  // .. + 7, so each store writes 64 contiguous bytes of a row
   const int ncol = n0 + 128 * (wave >> 2);
-  if (ncol >= N) return;
+  if (ncol >= N) return;  // uniform over the wave
+  typedef __attribute__((ext_vector_type(2))) unsigned u32x2;
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt) {
     const int m = m0 + 64 * (wave & 3) + 16 * mt + l16;
-    if (m < T) {
-      uint16_t* o = out + (size_t)m * N + ncol + 4 * g;
+    uint16_t* o = out + (size_t)m * N + ncol;
 #pragma unroll
-      for (int nt = 0; nt < 8; ++nt) {
-        const bf16x2 a = to_bf16x2(acc[nt][mt][0], acc[nt][mt][1]);
-        const bf16x2 b = to_bf16x2(acc[nt][mt][2], acc[nt][mt][3]);
-        *(bf16x4*)(o + 16 * nt) = bf16x4{a[0], a[1], b[0], b[1]};
-      }
+    for (int p = 0; p < 4; ++p) {
+      const f32x4 x0 = acc[2 * p][mt], x1 = acc[2 * p + 1][mt];
+      const bf16x2 a0 = to_bf16x2(x0[0], x0[1]), b0 = to_bf16x2(x0[2], x0[3]);
+      const bf16x2 a1 = to_bf16x2(x1[0], x1[1]), b1 = to_bf16x2(x1[2], x1[3]);
+      const u32x2 s0 = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(unsigned, a0),
+                                                        __builtin_bit_cast(unsigned, a1), false,
+                                                        false);
+      const u32x2 s1 = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(unsigned, b0),
+                                                        __builtin_bit_cast(unsigned, b1), false,
+                                                        false);
+      if (m < T)
+        *(i32x4*)(o + 16 * (2 * p + (g & 1)) + 8 * (g >> 1)) =
+            i32x4{(int)s0[0], (int)s1[0], (int)s0[1], (int)s1[1]};
     }
   }
 }
