@@ -290,25 +290,35 @@ __global__ void __launch_bounds__(pf::kThreads, 1) prefill_attention_kernel(cons
     __syncthreads();
   }
 
-  // ---- epilogue: lane (l16, g) holds columns 16 ct + 4 g .. + 3 of its row
+  // ---- epilogue: lane (l16, g) holds columns 16 ct + 4 g .. + 3 of its
+  //      row; a swap between 16-lane groups over tiles 2 c and 2 c + 1
+  //      leaves lane group g with 8 consecutive columns 16 (2 c + (g & 1)) +
+  //      8 (g >> 1) .. + 7, so each store writes 64 contiguous bytes of a row
+  typedef __attribute__((ext_vector_type(2))) unsigned u32x2;
 #pragma unroll
   for (int rt = 0; rt < 2; ++rt) {
     const int row = row_base + 16 * rt + l16;
     const float lt = wave_sum_x4(l_part[rt]);
-    if (row < n) {
-      const float inv = lt > 0.f ? 1.f / lt : 0.f;
-      uint16_t* op = p.o + ((size_t)(seq0 + row) * H + h) * kVD + 4 * g;
+    const float inv = lt > 0.f ? 1.f / lt : 0.f;
+    uint16_t* op = p.o + ((size_t)(seq0 + (row < n ? row : 0)) * H + h) * kVD;
 #pragma unroll
-      for (int ct = 0; ct < kCT; ++ct) {
-        const f32x4 v = o[rt][ct] * inv;
-        const bf16x2 a = to_bf16x2(v[0], v[1]);
-        const bf16x2 b = to_bf16x2(v[2], v[3]);
-        *(bf16x4*)(op + 16 * ct) = bf16x4{a[0], a[1], b[0], b[1]};
-      }
-      if (g == 0)
-        p.lse[(size_t)(seq0 + row) * H + h] =
-            lt > 0.f ? (m_used[rt] * sl2 + __builtin_amdgcn_logf(lt)) * kLn2 : -INFINITY;
+    for (int c = 0; c < kCT / 2; ++c) {
+      const f32x4 x0 = o[rt][2 * c] * inv, x1 = o[rt][2 * c + 1] * inv;
+      const bf16x2 a0 = to_bf16x2(x0[0], x0[1]), b0 = to_bf16x2(x0[2], x0[3]);
+      const bf16x2 a1 = to_bf16x2(x1[0], x1[1]), b1 = to_bf16x2(x1[2], x1[3]);
+      const u32x2 s0 = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(unsigned, a0),
+                                                        __builtin_bit_cast(unsigned, a1), false,
+                                                        false);
+      const u32x2 s1 = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(unsigned, b0),
+                                                        __builtin_bit_cast(unsigned, b1), false,
+                                                        false);
+      if (row < n)
+        *(i32x4*)(op + 16 * (2 * c + (g & 1)) + 8 * (g >> 1)) =
+            i32x4{(int)s0[0], (int)s1[0], (int)s0[1], (int)s1[1]};
     }
+    if (row < n && g == 0)
+      p.lse[(size_t)(seq0 + row) * H + h] =
+          lt > 0.f ? (m_used[rt] * sl2 + __builtin_amdgcn_logf(lt)) * kLn2 : -INFINITY;
   }
 }
 
