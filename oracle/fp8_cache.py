@@ -5,7 +5,7 @@ library shares no code with it.
 
 The pages use FP8 for matrix products, training and communication
 (DeepSeek-V3 hardware paper summary, section on FP8 mixed precision), not
-for the attention cache; storing the latent cache in FP8 is this build's
+for the attention cache; storing the latent cache in FP8 is this library's
 own extension.  Format, per token (656 bytes):
 
   [0, 512)    the 512 latent values as OCP FP8 E4M3 codes (1 sign, 4 exponent
