@@ -484,3 +484,33 @@ def test_graph_replays_equal_eager(mla, L, s_q, h_q):
     o, l = out.view(torch.int16).cpu().numpy().view(np.uint16), lse.cpu().numpy()
     ref_out, ref_lse = oracle.decode_ref(case, batches=[0, 1])
     compare(oracle.bf16_to_f64(o), l.astype(np.float64), ref_out, ref_lse, batches=[0, 1])
+
+
+def _random_cases(n, seed):
+    """Small random decode batches the oracle finishes quickly: lengths 0..400
+    (empty, single-token, page-edge and ragged), 1..3 query tokens, head
+    counts on both sides of every kernel's row limit, causal or not, and a
+    partition count from one to a few hundred."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    edges = [0, 1, 31, 32, 33, 63, 64, 65, 127, 128, 129]
+    out = []
+    for i in range(n):
+        batch = int(rng.integers(1, 7))
+        L = [int(rng.choice(edges)) if rng.random() < 0.4 else int(rng.integers(0, 401))
+             for _ in range(batch)]
+        s_q = int(rng.integers(1, 4))
+        h_q = int(rng.choice([1, 3, 8, 16, 20, 32, 48, 64, 128]))
+        causal = bool(rng.random() < 0.5)
+        num_cus = int(rng.choice([1, 3, 16, 77, 256, 300]))
+        out.append((L, s_q, h_q, causal, num_cus, seed * 100 + i))
+    return out
+
+
+@pytest.mark.parametrize("L,s_q,h_q,causal,num_cus,seed", _random_cases(24, 9001))
+def test_random_small_cases(mla, L, s_q, h_q, causal, num_cus, seed):
+    _say(f"[random] L={L} s_q={s_q} h_q={h_q} causal={causal} num_cus={num_cus} seed={seed}")
+    case = make_case(L, s_q, h_q, causal, seed=seed, pool_factor=1.5, poison_unused=True,
+                     poison_tail=True)
+    out, lse = run(mla, case, num_cus=num_cus)
+    ref_out, ref_lse = oracle.decode_ref(case)
+    compare(out, lse, ref_out, ref_lse)
