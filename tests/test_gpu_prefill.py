@@ -193,3 +193,37 @@ def test_expansion_refuses_a_huge_latent_stride(mla):
     big = torch.empty((2, (1 << 21) + 8), dtype=torch.bfloat16, device="cuda:0")
     with pytest.raises(mla.MlaError):
         mla.prefill_expand_kv(big, wk, wv)
+
+
+def _random_prompts(n, seed):
+    """Seeded small prompt mixes: 1..4 prompts of 0..400 tokens (with block
+    edges), 1..9 heads, causal or not."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    edges = [0, 1, 63, 64, 65, 255, 256, 257]
+    out = []
+    for i in range(n):
+        k = int(rng.integers(1, 5))
+        lens = [int(rng.choice(edges)) if rng.random() < 0.4 else int(rng.integers(1, 401))
+                for _ in range(k)]
+        if sum(lens) == 0:
+            lens[0] = 1
+        out.append((lens, int(rng.integers(1, 10)), bool(rng.random() < 0.7), seed * 100 + i))
+    return out
+
+
+@pytest.mark.parametrize("seqlens,h,causal,seed", _random_prompts(12, 7001))
+def test_prefill_random_mixes(mla, seqlens, h, causal, seed):
+    print(f"[prefill random] lengths {seqlens} heads {h} causal {causal} seed {seed}", flush=True)
+    case = make_prefill_case(seqlens, h, seed=seed)
+    kn_b, v_b, o_b, lse = _run(mla, case, causal)
+    lat = oracle.bf16_to_f64(case.latent)
+    c, r = lat[:, :512], lat[:, 512:]
+    q = oracle.bf16_to_f64(case.q)
+    wk, wv = oracle.bf16_to_f64(case.w_uk), oracle.bf16_to_f64(case.w_uv)
+    kn_ref, v_ref = pf.expand_kv(c, wk, wv)
+    _close(oracle.bf16_to_f64(kn_b), kn_ref)
+    _close(oracle.bf16_to_f64(v_b), v_ref)
+    kn, vv = oracle.bf16_to_f64(kn_b), oracle.bf16_to_f64(v_b)
+    o_ref, l_ref = pf.attention_ref(q, kn, r, vv, case.cu_seqlens, case.softmax_scale, causal)
+    _close(oracle.bf16_to_f64(o_b), o_ref)
+    assert np.abs(lse - l_ref).max() <= LSE_ATOL
