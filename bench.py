@@ -1010,14 +1010,16 @@ def main():
                                          3000 + k, dev),
             # the FP8 cache decode takes at most 16 rows: the memory-bound workload
             "fp8_cache": fp8_cache_rates(mla, c2, dev),
-            # more query tokens per sequence: 2 and 4 speculative tokens on
-            # the memory-bound workload's sequences (32 and 64 rows), and a
-            # 512-token chunk at 128 heads over a 4096-token cache
+            # more query tokens per sequence: 2, 4 and 8 speculative tokens
+            # on the memory-bound workload's sequences (32, 64 and 128 rows),
+            # and a 512-token chunk at 128 heads over a 4096-token cache
             "query_tokens": {
                 "speculative_s_q2": query_token_rates(
                     mla, [int(x) for x in c2.cache_seqlens], 2, 16, 4001, dev),
                 "speculative_s_q4": query_token_rates(
                     mla, [int(x) for x in c2.cache_seqlens], 4, 16, 4002, dev),
+                "speculative_s_q8": query_token_rates(
+                    mla, [int(x) for x in c2.cache_seqlens], 8, 16, 4004, dev),
                 "chunk_512x128": query_token_rates(mla, [4096], 512, 128, 4003, dev),
             },
             # MLA prefill in per-head form: one 4096-token prompt at 128 heads

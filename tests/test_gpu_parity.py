@@ -196,7 +196,8 @@ def test_edge_lengths(mla, h_q, s_q, causal):
 
 
 @pytest.mark.parametrize("s_q,h_q,causal", [(1, 8, False), (1, 20, False), (5, 7, True),
-                                             (3, 40, True), (4, 128, True), (16, 128, True)])
+                                             (3, 40, True), (8, 16, True), (4, 128, True),
+                                             (16, 128, True)])
 def test_row_shapes(mla, s_q, h_q, causal):
     """Row counts R = s_q * h_q that are not multiples of 16 (partial row tiles
     in every kernel variant), several row groups, and 2048 rows (32 row
