@@ -799,6 +799,37 @@ def machine_limits(mla, dev):
         if it:
             ts.append(e0.elapsed_time(e1))
     read_gbs = nbytes / (float(np.median(ts)) * 1e-3) / 1e9
+    # the 64-row decode's page copies alone (LDS-DMA, four-slot ring, two
+    # slots ahead, 256 workgroups): cycles per 36 KiB slot and the time from
+    # the end of a slot's issue to the end of the wait for it
+    ring = {}
+    rblocks, rsteps = 256, 2000
+    rsink = torch.empty(rblocks * 512, dtype=torch.int32, device=dev)
+    rclk = torch.zeros(2 * rblocks, dtype=torch.int64, device=dev)
+    for name, kind, slots in (("l2_resident_alone", 0, 2), ("l2_resident_beside_key_reads", 1, 2),
+                              ("l2_resident_beside_68_mfma_per_simd", 2, 2),
+                              ("hbm_stream_alone", 0, 200)):
+        assert rblocks * slots * 36864 <= nbytes
+        cyc, lat = [], []
+        for it in range(3):
+            rc = lib.mla_probe_copy_ring(kind, ctypes.c_void_p(buf.data_ptr()), slots, rsteps, rblocks,
+                                         ctypes.c_void_p(rsink.data_ptr()),
+                                         ctypes.c_void_p(rclk.data_ptr()), st())
+            torch.cuda.synchronize()
+            if rc:
+                raise RuntimeError(f"probe status {rc}")
+            if it:
+                c = rclk.cpu().numpy().reshape(rblocks, 2).astype(np.float64)
+                cyc.append(float(c[:, 0].mean()) / rsteps)
+                lat.append(float(c[:, 1].mean()))
+        per_slot = float(np.median(cyc))
+        ring[name] = {"cycles_per_slot": round(per_slot, 1),
+                      "bytes_per_clock_per_cu": round(36864 / per_slot, 1),
+                      "issue_to_landed_cycles": round(float(np.median(lat)), 1)}
+    ring["work"] = ("256 workgroups x 8 waves; waves 4-7 copy 36 KiB slots (nine 1 KiB LDS-DMA "
+                    "copies each) two slots ahead into a 4-slot ring, one barrier per slot; "
+                    "waves 0-3 idle, read 576 B of key fragments per lane, or run 68 bf16 "
+                    "16x16x32 MFMA per slot; 2 slots per workgroup stay in L2, 200 stream from HBM")
     del buf
     # matrix loop: 256 workgroups of 8 waves, 4 chains each
     mblocks, iters = 256, 20000
@@ -868,7 +899,8 @@ def machine_limits(mla, dev):
             "shader_clock_GHz_under_mfma": round(float(np.median(ghz)), 3),
             "spec_clock_GHz": 2.4,
             "lds_read_bytes_per_clock_per_cu": lds,
-            "matrix_beside_vector_work": issue}
+            "matrix_beside_vector_work": issue,
+            "page_copy_ring": ring}
 
 
 def trace_stats(path):

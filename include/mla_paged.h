@@ -408,6 +408,23 @@ mla_status_t mla_probe_lds(int32_t kind, int32_t iters, int32_t blocks, void* si
  * back to back means the two kinds of work do not overlap. */
 mla_status_t mla_probe_issue(int32_t kind, int32_t iters, int32_t blocks, void* sink,
                              void* clocks, hipStream_t stream);
+/* mla_probe_copy_ring: the 64-row decode's page copies on their own.  Each
+ * of `blocks` workgroups of 8 waves owns `slots` (2 .. 65536) consecutive
+ * 36 KiB slots of `src` (device, 16-byte aligned, at least blocks x slots x
+ * 36864 bytes, which the caller guarantees) and walks them cyclically for
+ * `steps` (3 .. 2^20) steps: waves 4-7 copy each slot into a four-slot LDS
+ * ring by LDS-DMA (nine 1 KiB copies per wave, two slots ahead, the decode's
+ * chunk layout), wait for their copies of slot i, then one barrier opens
+ * step i.  Waves 0-3: kind 0 only meet the barriers, kind 1 read the step's
+ * slot as the decode's score waves read key fragments (576 bytes per lane),
+ * kind 2 run 68 bf16 16x16x32 matrix instructions per step.  Writes blocks
+ * x 512 ints to `sink` and, per workgroup g, two 8-byte counts to `clocks`
+ * (device): the copying loop's shader-clock cycles (2 g) and the mean
+ * cycles from the end of a slot's issue to the end of the wait for it
+ * (2 g + 1).  With two slots per workgroup the data stays in L2; with
+ * hundreds it streams from HBM. */
+mla_status_t mla_probe_copy_ring(int32_t kind, const void* src, int32_t slots, int32_t steps,
+                                 int32_t blocks, void* sink, void* clocks, hipStream_t stream);
 
 /* Static, human-readable text of a status code. */
 const char* mla_status_string(mla_status_t status);

@@ -117,6 +117,8 @@ def load_library() -> ctypes.CDLL:
     lib.mla_probe_lds.restype = ctypes.c_int
     lib.mla_probe_issue.argtypes = [i32, i32, i32, vp, vp, vp]
     lib.mla_probe_issue.restype = ctypes.c_int
+    lib.mla_probe_copy_ring.argtypes = [i32, vp, i32, i32, i32, vp, vp, vp]
+    lib.mla_probe_copy_ring.restype = ctypes.c_int
     lib.mla_decode_step_noalloc.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32,
                                             vp, vp, vp]
     lib.mla_decode_step_noalloc.restype = ctypes.c_int

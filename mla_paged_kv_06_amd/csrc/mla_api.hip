@@ -21,6 +21,9 @@ extern "C" hipError_t mla_launch_probe_stream_read(const void* src, size_t bytes
                                                    int blocks, hipStream_t stream);
 extern "C" hipError_t mla_launch_probe_issue(int kind, int iters, int blocks, float* sink,
                                              unsigned long long* clk, hipStream_t stream);
+extern "C" hipError_t mla_launch_probe_copy_ring(int kind, const void* src, int slots, int steps,
+                                                 int blocks, int* sink, unsigned long long* clk,
+                                                 hipStream_t stream);
 extern "C" hipError_t mla_launch_probe_lds(int kind, int iters, int blocks, int* sink,
                                            unsigned long long* clk, hipStream_t stream);
 extern "C" hipError_t mla_launch_probe_mfma(int iters, int blocks, float* sink,
@@ -458,6 +461,17 @@ mla_status_t mla_probe_issue(int32_t kind, int32_t iters, int32_t blocks, void* 
     return MLA_ERR_INVALID_ARGUMENT;
   return mla_launch_probe_issue(kind, iters, blocks, (float*)sink, (unsigned long long*)clocks,
                                 stream) == hipSuccess
+             ? MLA_OK
+             : MLA_ERR_HIP;
+}
+
+mla_status_t mla_probe_copy_ring(int32_t kind, const void* src, int32_t slots, int32_t steps,
+                                 int32_t blocks, void* sink, void* clocks, hipStream_t stream) {
+  if (!src || ((uintptr_t)src & 15) || !sink || !clocks || kind < 0 || kind > 2 || slots < 2 ||
+      slots > (1 << 16) || steps < 3 || steps > (1 << 20) || blocks <= 0)
+    return MLA_ERR_INVALID_ARGUMENT;
+  return mla_launch_probe_copy_ring(kind, src, slots, steps, blocks, (int*)sink,
+                                    (unsigned long long*)clocks, stream) == hipSuccess
              ? MLA_OK
              : MLA_ERR_HIP;
 }

@@ -10,16 +10,23 @@
 //     8-byte reads of value fragments, 8 waves per compute unit;
 //   - matrix instructions in one wave of a SIMD beside plain vector work
 //     (fused multiply-adds or exponentials) in the other, and each alone:
-//     whether the two kinds of work share a SIMD's time or overlap.
+//     whether the two kinds of work share a SIMD's time or overlap;
+//   - the page copies of the 64-row decode on their own: four waves copy
+//     36 KiB slots HBM/L2 -> LDS by LDS-DMA into a four-slot ring, two slots
+//     ahead, one barrier per slot, with the other four waves idle, reading
+//     key fragments from LDS, or running matrix instructions beside them.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#pragma clang diagnostic ignored "-Winline-asm"
 
 namespace mla {
 
 typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
 typedef __attribute__((ext_vector_type(8))) __bf16 pbf16x8;
 typedef __attribute__((ext_vector_type(4))) float pf32x4;
+typedef __attribute__((ext_vector_type(4))) int i32x4p;
 
 constexpr int kStreamThreads = 256;
 constexpr int kStreamUnroll = 8;  // 16-byte loads in flight per lane
@@ -206,7 +213,140 @@ __global__ void __launch_bounds__(kIssueThreads)
   sink[(size_t)blockIdx.x * kIssueThreads + tid] = s;
 }
 
+constexpr int kRingSlot = 36864;  // 32 tokens x 1152 bytes
+constexpr int kRingThreads = 512;
+constexpr int kRingCopies = 9;    // 1 KiB copies per copying wave and slot
+
+// One wave-wide copy, 16 bytes per lane, of voff + soff of the resource to
+// LDS address lds + 16 lane (M0 carries the LDS base; no compiled code in
+// this kernel uses M0).
+__device__ __forceinline__ void ring_copy16(__attribute__((address_space(3))) char* lds, int voff,
+                                            i32x4p rsrc, int soff) {
+  const int m0 = __builtin_amdgcn_readfirstlane((int)(size_t)lds);
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 4\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               :
+               : "s"(m0), "v"(voff), "s"(rsrc), "s"(soff)
+               : "memory", "m0");
+}
+
+template <int kImm>
+__device__ __forceinline__ void ring_wait() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(kImm);
+  asm volatile("" ::: "memory");
+}
+
+// Workgroup g copies slots s % slots of its own region src + g * slots *
+// 36864, in the decode's order: copying wave c (waves 4..7) moves 8-token
+// block c of a slot (nine 1 KiB LDS-DMA loads, chunk offsets XOR-swizzled
+// by token as the decode lays them out) into ring buffer s & 3, two slots
+// ahead, and waits for its copies of slot i before the barrier that opens
+// step i.  kKind 0: waves 0..3 only meet the barriers; 1: they read the
+// step's slot as the score waves do (36 16-byte key-fragment reads per lane);
+// 2: they run 68 bf16 16x16x32 matrix instructions per step (a 64-row
+// step's matrix work on one SIMD).  Wave 4 of each workgroup records its
+// loop's shader-clock cycles (clk[2 g]) and the mean time from the end of a
+// slot's issue to the end of the wait for it (clk[2 g + 1]).
+template <int kKind>
+__global__ void __launch_bounds__(kRingThreads, 1)
+    probe_copy_ring_kernel(const char* __restrict__ src, int slots, int steps,
+                           int* __restrict__ sink, unsigned long long* __restrict__ clk) {
+  typedef __attribute__((address_space(3))) char lds_char;
+  __shared__ __attribute__((aligned(1024))) char ring_[4 * kRingSlot];
+  lds_char* ring = (lds_char*)ring_;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const char* base = src + (size_t)blockIdx.x * slots * kRingSlot;
+  int acc = 0;
+  if (wave >= 4) {
+    const int c = wave - 4, blk = c * 9216;
+    int coff[kRingCopies];
+#pragma unroll
+    for (int k = 0; k < kRingCopies; ++k) {
+      const int pc = 64 * k + lane, t = pc / 72, ch = pc - t * 72;
+      coff[k] = t * 1152 + 16 * (ch ^ (t & 7));
+    }
+    auto rsrc = [&](int s) __attribute__((always_inline)) {
+      const unsigned long long a = (unsigned long long)(base + (size_t)(s % slots) * kRingSlot);
+      return i32x4p{__builtin_amdgcn_readfirstlane((int)(unsigned)a),
+                    __builtin_amdgcn_readfirstlane((int)((a >> 32) & 0xFFFF)), kRingSlot,
+                    0x00020000};
+    };
+    const unsigned long long t0 = __builtin_readcyclecounter();
+    unsigned long long issued[2] = {0, 0}, lat = 0;
+    for (int s = 0; s < 2; ++s) {
+      const i32x4p r = rsrc(s);
+#pragma unroll
+      for (int k = 0; k < kRingCopies; ++k)
+        ring_copy16(ring + s * kRingSlot + blk + 1024 * k, coff[k], r, blk);
+    }
+    for (int i = 0; i < steps; ++i) {
+      ring_wait<0x0F70 | 9>();  // this wave's copies of slot i landed
+      const unsigned long long tl = __builtin_readcyclecounter();
+      if (i >= 2) lat += tl - issued[i & 1];
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      const i32x4p r = rsrc(i + 2);
+#pragma unroll
+      for (int k = 0; k < kRingCopies; ++k)
+        ring_copy16(ring + ((i + 2) & 3) * kRingSlot + blk + 1024 * k, coff[k], r, blk);
+      issued[i & 1] = __builtin_readcyclecounter();
+    }
+    ring_wait<0x0F70>();  // nothing may still fly when the wave ends
+    if (c == 0 && lane == 0) {
+      clk[2 * blockIdx.x] = __builtin_readcyclecounter() - t0;
+      clk[2 * blockIdx.x + 1] = steps > 2 ? lat / (unsigned long long)(steps - 2) : 0;
+    }
+  } else {
+    pbf16x8 q;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) q[k] = (__bf16)(0.001f * (float)(lane + k));
+    const int l16 = lane & 15, g = lane >> 4, sw = l16 & 7;
+    const int kl = l16 * 1152 + 16 * (g ^ (sw & 3));
+    const int ke = kl + ((sw & 4) ? 64 : 0), ko = kl - ((sw & 4) ? 64 : 0);
+    for (int i = 0; i < steps; ++i) {
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      if constexpr (kKind == 1) {
+        const lds_char* kb = ring + (i & 3) * kRingSlot;
+        u32x4 x = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int ks = 0; ks < 18; ++ks) {
+          x ^= *(const __attribute__((address_space(3))) u32x4*)(kb + ((ks & 1) ? ko : ke) + 64 * ks);
+          x ^= *(const __attribute__((address_space(3))) u32x4*)(kb + ((ks & 1) ? ko : ke) + 64 * ks +
+                                                               16 * 1152);
+        }
+        acc ^= (int)(x[0] ^ x[1] ^ x[2] ^ x[3]);
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // reads done before the next copies land
+      } else if constexpr (kKind == 2) {
+        pf32x4 cc[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) cc[k] = pf32x4{(float)k, 0.f, 0.f, (float)i};
+#pragma unroll
+        for (int r = 0; r < 17; ++r)
+#pragma unroll
+          for (int k = 0; k < 4; ++k) cc[k] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(q, q, cc[k], 0, 0, 0);
+        acc += (int)(cc[0][0] + cc[1][1] + cc[2][2] + cc[3][3]);
+      }
+    }
+  }
+  sink[(size_t)blockIdx.x * kRingThreads + threadIdx.x] = acc;
+}
+
 }  // namespace mla
+
+extern "C" hipError_t mla_launch_probe_copy_ring(int kind, const void* src, int slots, int steps,
+                                                 int blocks, int* sink, unsigned long long* clk,
+                                                 hipStream_t stream) {
+  const dim3 grid(blocks), block(mla::kRingThreads);
+  const char* s = (const char*)src;
+  switch (kind) {
+    case 0: hipLaunchKernelGGL(mla::probe_copy_ring_kernel<0>, grid, block, 0, stream, s, slots, steps, sink, clk); break;
+    case 1: hipLaunchKernelGGL(mla::probe_copy_ring_kernel<1>, grid, block, 0, stream, s, slots, steps, sink, clk); break;
+    default: hipLaunchKernelGGL(mla::probe_copy_ring_kernel<2>, grid, block, 0, stream, s, slots, steps, sink, clk); break;
+  }
+  return hipGetLastError();
+}
 
 extern "C" hipError_t mla_launch_probe_issue(int kind, int iters, int blocks, float* sink,
                                              unsigned long long* clk, hipStream_t stream) {

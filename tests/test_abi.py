@@ -220,3 +220,20 @@ def test_probe_arguments_are_checked_on_the_host(lib):
     assert lib.mla_probe_issue(0, 10, 0, dummy, dummy, None) == 1   # no workgroups
     assert lib.mla_probe_issue(0, 10, 1, None, dummy, None) == 1    # no sink
     assert lib.mla_probe_issue(0, 10, 1, dummy, None, None) == 1    # no clocks
+
+
+def test_copy_ring_probe_arguments_are_checked_on_the_host(lib):
+    """The page-copy probe refuses bad arguments before any HIP call."""
+    vp, i32 = ctypes.c_void_p, ctypes.c_int32
+    lib.mla_probe_copy_ring.argtypes = [i32, vp, i32, i32, i32, vp, vp, vp]
+    lib.mla_probe_copy_ring.restype = i32
+    d = vp(256)  # never dereferenced: the checks fail first
+    assert lib.mla_probe_copy_ring(3, d, 2, 10, 1, d, d, None) == 1       # no such kind
+    assert lib.mla_probe_copy_ring(-1, d, 2, 10, 1, d, d, None) == 1
+    assert lib.mla_probe_copy_ring(0, None, 2, 10, 1, d, d, None) == 1    # no buffer
+    assert lib.mla_probe_copy_ring(0, vp(264), 2, 10, 1, d, d, None) == 1  # not 16-byte aligned
+    assert lib.mla_probe_copy_ring(0, d, 1, 10, 1, d, d, None) == 1       # the ring needs 2 slots
+    assert lib.mla_probe_copy_ring(0, d, 2, 2, 1, d, d, None) == 1        # too few steps
+    assert lib.mla_probe_copy_ring(0, d, 2, 10, 0, d, d, None) == 1       # no workgroups
+    assert lib.mla_probe_copy_ring(0, d, 2, 10, 1, None, d, None) == 1    # no sink
+    assert lib.mla_probe_copy_ring(0, d, 2, 10, 1, d, None, None) == 1    # no clocks
