@@ -196,13 +196,16 @@ __global__ void __launch_bounds__(256, 2) absorb_kernel(const uint16_t* __restri
 
 // Prefill expansion as one matrix product per weight:
 //   C[t][n] = sum_k latent[t][k] W[n][k],  n = 128 h + d,  k < 512,
-// k_nope (W_UK) and v (W_UV) both [T][H][128] = [T][N].  A workgroup of 8
-// waves owns a 256 x 256 tile of C (wave w: rows 64 (w & 3) .., columns
-// 128 (w >> 2) ..; 4 x 8 MFMA 16x16x32 tiles, 128 accumulators).  The
-// contraction runs in 8 stages of 64 values (two MFMA k-steps); each
+// k_nope (W_UK) and v (W_UV) both [T][H][128] = [T][N].  One workgroup of 8
+// waves per compute unit walks 256 x 256 tiles of C (wave w: rows 64 (w & 3)
+// .., columns 128 (w >> 2) ..; 4 x 8 MFMA 16x16x32 tiles, 128 accumulators).
+// The contraction runs in 8 stages of 64 values (two MFMA k-steps); each
 // stage's 256 x 64 slices of the latents and of W (32 KiB each) are copied
 // HBM -> LDS by LDS-DMA (buffer_load ... lds, eight 1 KiB copies per wave)
-// into the other of two buffers while the current stage computes.  LDS
+// into the other of two buffers while the current stage computes, and the
+// last stage of a tile copies the first of the workgroup's next tile, so
+// neither a tile's first copies nor its stores leave the matrix cores idle
+// between tiles.  LDS
 // rows are 128 bytes; the 16-byte chunk c of row r sits at c ^ (r & 7), so
 // the rows one fragment read touches fall on distinct banks.  Buffer
 // resources bounded at the last row (T, N) make rows past the ends read as
@@ -240,20 +243,14 @@ __device__ __forceinline__ void ex_wait() {
 __global__ void __launch_bounds__(ex::kThreads, 1)
     expand_gemm_kernel(const uint16_t* __restrict__ latent, int latent_stride, int T,
                        const uint16_t* __restrict__ w0, const uint16_t* __restrict__ w1, int N,
-                       uint16_t* __restrict__ out0, uint16_t* __restrict__ out1) {
+                       uint16_t* __restrict__ out0, uint16_t* __restrict__ out1, int n_tiles,
+                       int tiles_m, int tiles_n) {
   using namespace ex;
   __shared__ __attribute__((aligned(1024))) char ring_[kRing * 2 * kSliceB];
   MLA_LDS char* ring = (MLA_LDS char*)ring_;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15, g = lane >> 4;
-  const int m0 = blockIdx.x * kBM;
-  const int n0 = blockIdx.y * kBN;
-  const uint16_t* w = blockIdx.z ? w1 : w0;
-  uint16_t* out = blockIdx.z ? out1 : out0;
-  const int rows_a = min(kBM, T - m0), rows_b = min(kBN, N - n0);
-  const i32x4 ra = ex_rsrc(latent + (size_t)m0 * latent_stride, rows_a * latent_stride * 2);
-  const i32x4 rb = ex_rsrc(w + (size_t)n0 * kDv, rows_b * kDv * 2);
   // this wave's copies of a stage: 1 KiB pieces 4 w .. 4 w + 3 of the A and
   // of the B slice (piece i, lane l: row 8 i + l / 8, physical chunk l & 7)
   int va[4], vb[4];
@@ -264,8 +261,25 @@ __global__ void __launch_bounds__(ex::kThreads, 1)
     va[u] = row * latent_stride * 2 + 16 * lc;
     vb[u] = row * kDv * 2 + 16 * lc;
   }
-  auto issue = [&](int st) __attribute__((always_inline)) {
-    MLA_LDS char* buf = ring + (st & (kRing - 1)) * 2 * kSliceB;
+  // tiles of this workgroup: blockIdx.x, + gridDim.x, ...  (tile id: m
+  // fastest, then n, then the weight); with a grid that is a multiple of
+  // tiles_m every tile of a workgroup shares its latent rows
+  struct Tile {
+    int m0, n0, z;
+  };
+  auto tile_of = [&](int id) __attribute__((always_inline)) {
+    Tile t;
+    t.m0 = (id % tiles_m) * kBM;
+    t.n0 = ((id / tiles_m) % tiles_n) * kBN;
+    t.z = id / (tiles_m * tiles_n);
+    return t;
+  };
+  auto issue = [&](const Tile& t, int st, int slot) __attribute__((always_inline)) {
+    const uint16_t* w = t.z ? w1 : w0;
+    const int rows_a = min(kBM, T - t.m0), rows_b = min(kBN, N - t.n0);
+    const i32x4 ra = ex_rsrc(latent + (size_t)t.m0 * latent_stride, rows_a * latent_stride * 2);
+    const i32x4 rb = ex_rsrc(w + (size_t)t.n0 * kDv, rows_b * kDv * 2);
+    MLA_LDS char* buf = ring + slot * 2 * kSliceB;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       ex_copy16(buf + 1024 * (4 * wave + u), va[u], ra, st * kBK * 2);
@@ -279,63 +293,79 @@ __global__ void __launch_bounds__(ex::kThreads, 1)
   const int fb0 = kSliceB + (128 * (wave >> 2) + l16) * 128 + 16 * (g ^ (l16 & 7));
   const int fb1 = kSliceB + (128 * (wave >> 2) + l16) * 128 + 16 * ((4 + g) ^ (l16 & 7));
 
-  f32x4 acc[8][4];
+  int id = blockIdx.x;
+  if (id >= n_tiles) return;
+  Tile cur = tile_of(id);
+  issue(cur, 0, 0);
+  int gstage = 0;  // stages computed by this workgroup so far (ring position)
+  for (;;) {
+    const int next_id = id + (int)gridDim.x;
+    const bool has_next = next_id < n_tiles;
+    const Tile nxt = tile_of(has_next ? next_id : id);
+    f32x4 acc[8][4];
 #pragma unroll
-  for (int nt = 0; nt < 8; ++nt)
+    for (int nt = 0; nt < 8; ++nt)
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) acc[nt][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  issue(0);
-  for (int st = 0; st < kStages; ++st) {
-    ex_wait<0x0F70>();             // this wave's copies of stage st landed
-    __builtin_amdgcn_s_barrier();  // every wave's copies landed; stage st - 1 read
-    asm volatile("" ::: "memory");
-    if (st + 1 < kStages) issue(st + 1);
-    const MLA_LDS char* buf = ring + (st & (kRing - 1)) * 2 * kSliceB;
+      for (int mt = 0; mt < 4; ++mt) acc[nt][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int st = 0; st < kStages; ++st, ++gstage) {
+      ex_wait<0x0F70>();             // this wave's copies of this stage landed
+      __builtin_amdgcn_s_barrier();  // every wave's copies landed; the last stage read
+      asm volatile("" ::: "memory");
+      // the next stage: of this tile, or the first of the next one
+      if (st + 1 < kStages)
+        issue(cur, st + 1, (gstage + 1) & (kRing - 1));
+      else if (has_next)
+        issue(nxt, 0, (gstage + 1) & (kRing - 1));
+      const MLA_LDS char* buf = ring + (gstage & (kRing - 1)) * 2 * kSliceB;
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      bf16x8 af[4], bf[8];
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-        af[mt] = *(const MLA_LDS bf16x8*)(buf + (ks ? fa1 : fa0) + 2048 * mt);
-#pragma unroll
-      for (int nt = 0; nt < 8; ++nt)
-        bf[nt] = *(const MLA_LDS bf16x8*)(buf + (ks ? fb1 : fb0) + 2048 * nt);
-#pragma unroll
-      for (int nt = 0; nt < 8; ++nt)
+      for (int ks = 0; ks < 2; ++ks) {
+        bf16x8 af[4], bf[8];
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt)
-          acc[nt][mt] =
-              __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf[nt], af[mt], acc[nt][mt], 0, 0, 0);
-    }
-  }
-  // lane (g, l16) holds columns 4 g .. 4 g + 3 of each 16-column tile, row
-  // l16; a swap between 16-lane groups over tiles 2 p and 2 p + 1 leaves
-  // lane group g with 8 consecutive columns 16 (2 p + (g & 1)) + 8 (g >> 1)
-  // .. + 7, so each store writes 64 contiguous bytes of a row
-  const int ncol = n0 + 128 * (wave >> 2);
-  if (ncol >= N) return;  // uniform over the wave
-  typedef __attribute__((ext_vector_type(2))) unsigned u32x2;
+          af[mt] = *(const MLA_LDS bf16x8*)(buf + (ks ? fa1 : fa0) + 2048 * mt);
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt) {
-    const int m = m0 + 64 * (wave & 3) + 16 * mt + l16;
-    uint16_t* o = out + (size_t)m * N + ncol;
+        for (int nt = 0; nt < 8; ++nt)
+          bf[nt] = *(const MLA_LDS bf16x8*)(buf + (ks ? fb1 : fb0) + 2048 * nt);
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const f32x4 x0 = acc[2 * p][mt], x1 = acc[2 * p + 1][mt];
-      const bf16x2 a0 = to_bf16x2(x0[0], x0[1]), b0 = to_bf16x2(x0[2], x0[3]);
-      const bf16x2 a1 = to_bf16x2(x1[0], x1[1]), b1 = to_bf16x2(x1[2], x1[3]);
-      const u32x2 s0 = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(unsigned, a0),
-                                                        __builtin_bit_cast(unsigned, a1), false,
-                                                        false);
-      const u32x2 s1 = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(unsigned, b0),
-                                                        __builtin_bit_cast(unsigned, b1), false,
-                                                        false);
-      if (m < T)
-        *(i32x4*)(o + 16 * (2 * p + (g & 1)) + 8 * (g >> 1)) =
-            i32x4{(int)s0[0], (int)s1[0], (int)s0[1], (int)s1[1]};
+        for (int nt = 0; nt < 8; ++nt)
+#pragma unroll
+          for (int mt = 0; mt < 4; ++mt)
+            acc[nt][mt] =
+                __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf[nt], af[mt], acc[nt][mt], 0, 0, 0);
+      }
     }
+    // lane (g, l16) holds columns 4 g .. 4 g + 3 of each 16-column tile, row
+    // l16; a swap between 16-lane groups over tiles 2 p and 2 p + 1 leaves
+    // lane group g with 8 consecutive columns 16 (2 p + (g & 1)) + 8 (g >> 1)
+    // .. + 7, so each store writes 64 contiguous bytes of a row
+    const int ncol = cur.n0 + 128 * (wave >> 2);
+    uint16_t* out = cur.z ? out1 : out0;
+    typedef __attribute__((ext_vector_type(2))) unsigned u32x2;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      const int m = cur.m0 + 64 * (wave & 3) + 16 * mt + l16;
+      uint16_t* o = out + (size_t)m * N + ncol;
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const f32x4 x0 = acc[2 * p][mt], x1 = acc[2 * p + 1][mt];
+        const bf16x2 a0 = to_bf16x2(x0[0], x0[1]), b0 = to_bf16x2(x0[2], x0[3]);
+        const bf16x2 a1 = to_bf16x2(x1[0], x1[1]), b1 = to_bf16x2(x1[2], x1[3]);
+        const u32x2 s0 = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(unsigned, a0),
+                                                          __builtin_bit_cast(unsigned, a1), false,
+                                                          false);
+        const u32x2 s1 = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(unsigned, b0),
+                                                          __builtin_bit_cast(unsigned, b1), false,
+                                                          false);
+        if (m < T && ncol < N)
+          *(i32x4*)(o + 16 * (2 * p + (g & 1)) + 8 * (g >> 1)) =
+              i32x4{(int)s0[0], (int)s1[0], (int)s0[1], (int)s1[1]};
+      }
+    }
+    if (!has_next) break;
+    id = next_id;
+    cur = nxt;
   }
+  ex_wait<0x0F70>();  // nothing may still fly when the wave ends
 }
 
 // tiles in flight ahead of the one computed, per wave (registers: rows
@@ -398,8 +428,14 @@ extern "C" hipError_t mla_launch_prefill_expand(const uint16_t* latent, int late
                                                 uint16_t* k_nope, uint16_t* v, hipStream_t stream) {
   using namespace mla;
   const int N = H * kNope;
-  const dim3 grid((T + ex::kBM - 1) / ex::kBM, (N + ex::kBN - 1) / ex::kBN, 2);
-  hipLaunchKernelGGL(expand_gemm_kernel, grid, dim3(ex::kThreads), 0, stream, latent,
-                     latent_stride, T, w_uk, w_uv, N, k_nope, v);
+  const int tiles_m = (T + ex::kBM - 1) / ex::kBM, tiles_n = (N + ex::kBN - 1) / ex::kBN;
+  const int n_tiles = tiles_m * tiles_n * 2;
+  // persistent workgroups, one per compute unit, a multiple of tiles_m so
+  // that each keeps its latent rows
+  int grid = 256 / tiles_m * tiles_m;
+  if (grid < tiles_m) grid = tiles_m;
+  if (grid > n_tiles) grid = n_tiles;
+  hipLaunchKernelGGL(expand_gemm_kernel, dim3(grid), dim3(ex::kThreads), 0, stream, latent,
+                     latent_stride, T, w_uk, w_uv, N, k_nope, v, n_tiles, tiles_m, tiles_n);
   return hipGetLastError();
 }
